@@ -1,0 +1,161 @@
+/*
+ * mx.h -- C ABI of libmx: OCP-MX micro-scaling quantization, the fixed-sign
+ * 32-point block-Hadamard rotation, and the MX-scaled GEMM, for AMD gfx950
+ * (Instinct MI355X).
+ *
+ * What the calls compute, and where it is stated:
+ *   - MX micro-scaling (FP4-training article on hzrcw.cc, section 02: the tensor
+ *     is cut into small blocks, each with its own dynamic scaling exponent;
+ *     MXFP4 is an OCP open format, section 04).  Block size 32 along the
+ *     reduction dimension (MindSpeed-LLM FSDP2 quantization page: recipe
+ *     dynamic_MX-1-1-32 and --model.quant_block_size 32).
+ *   - Element formats E4M3 and E5M2 (Lumen page, section 1: E4M3 for
+ *     precision, E5M2 for range) and E2M1 (MXFP4), OCP encodings: E4M3 "FN"
+ *     (bias 7, max 448, no infinities), E5M2 (bias 15, max normal 57344),
+ *     E2M1 (bias 1, max 6).  Shared scale: one E8M0 byte per block,
+ *       S = clamp(floor(log2 amax) - emax, -127, 127) + 127,
+ *     emax = 8 (E4M3), 15 (E5M2), 2 (E2M1); elements are v * 2^-(S-127),
+ *     rounded to nearest (ties to even) and saturated to +-max normal.
+ *   - The deterministic fixed-sign Hadamard rotation on the weight-gradient
+ *     path (FP4-training article, section 02: one fixed orthogonal transform
+ *     in place of random rotations), applied along tokens before the FP4
+ *     quantization of both weight-gradient operands.
+ *   - The quantized GEMMs of a linear layer (FP4-training article, section
+ *     02: forward, activation-gradient and weight-gradient GEMMs), which the
+ *     Primus page names as the dominant training cost (GEMM tuning section).
+ *
+ * Conventions shared by every call:
+ *   - All data pointers are DEVICE pointers, allocated and freed by the
+ *     caller.  The library allocates nothing and keeps no per-call state.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default (null)
+ *     stream.  Calls are asynchronous on that stream and never synchronize.
+ *   - Inputs are read only.  Outputs are overwritten completely (no
+ *     accumulation).  Inputs and outputs must not overlap.
+ *   - bf16 inputs are row-major with a leading dimension `ldx` (elements
+ *     between the starts of consecutive rows, ldx >= cols).
+ *   - Outputs are dense row-major:
+ *       FP8 codes   : one byte per element;
+ *       E2M1 codes  : two elements per byte, element 2i in bits 3:0 and
+ *                     element 2i+1 in bits 7:4;
+ *       scales      : one E8M0 byte per 32-element block.
+ *   - A block that holds an Inf or NaN gets scale 0xFF (E8M0 NaN) and all
+ *     element codes 0.  An all-zero block gets scale 0x00.  The sign of zero
+ *     is kept (-0 -> 0x80 for FP8, 0x8 for E2M1).
+ *   - A size of 0 is a valid empty call: nothing is read or written (except
+ *     mx_gemm with K == 0, which writes C = 0), and pointers may be NULL.
+ *
+ * Errors (no call throws, no call aborts):
+ *   MX_ERR_INVALID_ARG  bad argument, detected on the host before any HIP
+ *                       call: NULL pointer with a non-empty size, negative
+ *                       size, a blocked dimension not a multiple of 32,
+ *                       ldx < cols, ldc < N, unknown enum value, or
+ *                       operand and output buffers that overlap.
+ *   MX_ERR_UNSUPPORTED  the current device is not gfx950, or an index range
+ *                       exceeds what the kernels address (more than 2^31
+ *                       blocks or rows in one call).
+ *   MX_ERR_HIP          a HIP runtime call or kernel launch failed.
+ *   Faults inside a kernel surface at the caller's next synchronization.
+ */
+#ifndef MX_H
+#define MX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MX_OK = 0,
+    MX_ERR_INVALID_ARG = 1,
+    MX_ERR_UNSUPPORTED = 2,
+    MX_ERR_HIP = 3
+} mx_status_t;
+
+typedef enum {
+    MX_E4M3 = 0, /* FP8 1-4-3, bias 7, max 448       */
+    MX_E5M2 = 1, /* FP8 1-5-2, bias 15, max 57344    */
+    MX_E2M1 = 2  /* FP4 1-2-1, bias 1, max 6, packed */
+} mx_format_t;
+
+typedef enum {
+    MX_OUT_F32 = 0, /* fp32 output                          */
+    MX_OUT_BF16 = 1 /* bf16 output, fp32 result rounded RNE */
+} mx_out_t;
+
+/*
+ * mx_quantize -- row mode.  Block b of row r is x[r, 32b .. 32b+31].
+ *   x_bf16  [rows x ldx] bf16, reads the first `cols` of each row
+ *   cols    multiple of 32
+ *   codes   [rows x cols] bytes (E4M3/E5M2) or [rows x cols/2] (E2M1)
+ *   scales  [rows x cols/32] E8M0 bytes
+ * This is the Fprop operand quantizer (activations and weights stored with
+ * the reduction dimension contiguous) and the Dgrad quantizer of the output
+ * gradient.
+ */
+mx_status_t mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                        mx_format_t fmt, void *codes, void *scales, void *stream);
+
+/*
+ * mx_quantize_transpose -- transposed mode.  Block b of column c is
+ * x[32b .. 32b+31, c]; it becomes block b of output row c, so the output is
+ * the MX form of x^T with `rows` as its contiguous (reduction) dimension.
+ *   rows    multiple of 32
+ *   codes   [cols x rows] bytes (E4M3/E5M2) or [cols x rows/2] (E2M1)
+ *   scales  [cols x rows/32]
+ * Used for operands whose reduction dimension is strided in storage: the
+ * weight in Dgrad (reduction over N_out) and, without rotation, the two
+ * weight-gradient operands (reduction over tokens).
+ */
+mx_status_t mx_quantize_transpose(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                                  mx_format_t fmt, void *codes, void *scales, void *stream);
+
+/*
+ * mx_hadamard32_quantize -- transposed mode after the fixed-sign block
+ * rotation.  For each column c and each 32-row block b, with
+ * x_i = x[32b + i, c] widened to fp32:
+ *     x_i <- -x_i  where bit i of sign_mask is set,
+ *     five butterfly stages h = 1, 2, 4, 8, 16, each replacing
+ *     (x_j, x_{j+h}) by (x_j + x_{j+h}, x_j - x_{j+h}) for every j with
+ *     (j & h) == 0, one fp32 rounding per operation,
+ *     y_i = x_i * c with c = 0x3E3504F3 = RN_fp32(1/sqrt(32)),
+ * i.e. y = c * H32 * diag(s) * x with H32 the Sylvester-Hadamard matrix.
+ * y (fp32, no bf16 rounding) is then quantized as block b of output row c,
+ * with the same output layout as mx_quantize_transpose.  Rotation blocks
+ * coincide with the MX blocks.  sign_mask = 0 is the plain Sylvester
+ * rotation.  Results are bit-identical for every launch configuration.
+ */
+mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                                   uint32_t sign_mask, mx_format_t fmt, void *codes, void *scales,
+                                   void *stream);
+
+/*
+ * mx_gemm -- C[m, n] = sum_k A[m, k] * B[n, k] over two MX operands, both
+ * with the reduction dimension K contiguous ("TN"):
+ *   a_codes [M x K] (FP8) or [M x K/2] (E2M1), a_scales [M x K/32]
+ *   b_codes [N x K] (FP8) or [N x K/2] (E2M1), b_scales [N x K/32]
+ *   A[m, k] = decode(code) * 2^(S - 127), same for B
+ *   K       multiple of 32
+ *   c       [M x ldc] fp32 or bf16 (per `out`), ldc >= N
+ * Products are formed by the gfx950 block-scaled matrix instructions and
+ * accumulated in fp32 in steps of 64 along K.  Fprop: A = X, B = W.
+ * Dgrad: A = dY, B = W^T (from mx_quantize_transpose).  Wgrad: A = dY^T,
+ * B = X^T (both from mx_hadamard32_quantize or mx_quantize_transpose).
+ * Any pair of formats is accepted.
+ */
+mx_status_t mx_gemm(const void *a_codes, const void *a_scales, mx_format_t fa,
+                    const void *b_codes, const void *b_scales, mx_format_t fb,
+                    int64_t M, int64_t N, int64_t K, void *c, mx_out_t out, int64_t ldc,
+                    void *stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char *mx_status_string(mx_status_t s);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int mx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_H */

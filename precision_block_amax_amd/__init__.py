@@ -1,0 +1,174 @@
+"""precision_block_amax_amd -- Python binding of libmx (include/mx.h) for AMD MI355X.
+
+OCP-MX micro-scaling quantization (block 32, E8M0 scales, E4M3 / E5M2 / E2M1
+elements), the fixed-sign 32-point block-Hadamard rotation used on the
+weight-gradient path, and the MX-scaled GEMM, as hand-written gfx950 HIP
+kernels behind a C ABI.
+
+This module only marshals arguments: it checks tensor shapes, dtypes and
+devices, allocates outputs with torch (device memory and streams are all
+torch is used for), and calls the library on the current HIP stream.  Every
+step of the computation runs in libmx.so; if the library is missing, loading
+fails loudly.  Build it with ``python -m precision_block_amax_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple, Union
+
+import torch
+
+__all__ = [
+    "E4M3", "E5M2", "E2M1", "MXError", "lib", "library_path", "code_cols",
+    "quantize", "quantize_transpose", "hadamard32_quantize", "gemm",
+]
+
+E4M3, E5M2, E2M1 = 0, 1, 2
+_FORMATS = {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1, E4M3: E4M3, E5M2: E5M2, E2M1: E2M1}
+OUT_F32, OUT_BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmx.so")
+_lib = None
+
+
+class MXError(RuntimeError):
+    """a libmx call returned a status other than MX_OK"""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """the loaded libmx.so (raises if it has not been built)"""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise MXError("libmx.so not found at %s; build it with "
+                          "`python -m precision_block_amax_amd.build`" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        P, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+        L.mx_quantize.argtypes = [P, i64, i64, i64, i32, P, P, P]
+        L.mx_quantize_transpose.argtypes = [P, i64, i64, i64, i32, P, P, P]
+        L.mx_hadamard32_quantize.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
+        L.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
+        for fn in (L.mx_quantize, L.mx_quantize_transpose, L.mx_hadamard32_quantize, L.mx_gemm):
+            fn.restype = ctypes.c_int
+        L.mx_status_string.argtypes = [ctypes.c_int]
+        L.mx_status_string.restype = ctypes.c_char_p
+        L.mx_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _fmt(f: Union[str, int]) -> int:
+    try:
+        return _FORMATS[f.lower() if isinstance(f, str) else f]
+    except KeyError:
+        raise ValueError("unknown MX format %r" % (f,)) from None
+
+
+def code_cols(n: int, fmt: Union[str, int]) -> int:
+    """bytes holding n elements of a row"""
+    return n // 2 if _fmt(fmt) == E2M1 else n
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MXError(lib().mx_status_string(status).decode())
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _check_bf16_2d(x: torch.Tensor) -> None:
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("expected a 2-D bf16 tensor on a GPU")
+    if x.stride(1) != 1 and x.numel() > 0:
+        raise ValueError("the last dimension must be contiguous")
+
+
+def _outputs(device, rows_out: int, k: int, fmt: int, out) -> Tuple[torch.Tensor, torch.Tensor]:
+    shape_c, shape_s = (rows_out, code_cols(k, fmt)), (rows_out, k // 32)
+    if out is None:
+        return (torch.empty(shape_c, dtype=torch.uint8, device=device),
+                torch.empty(shape_s, dtype=torch.uint8, device=device))
+    codes, scales = out
+    for t, shp in ((codes, shape_c), (scales, shape_s)):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shp or not t.is_contiguous() or t.device != device:
+            raise ValueError("output buffer must be contiguous uint8 of shape %s" % (shp,))
+    return codes, scales
+
+
+def _ldx(x: torch.Tensor) -> int:
+    return x.stride(0) if x.shape[0] > 1 else x.shape[1]
+
+
+def quantize(x: torch.Tensor, fmt, out=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mx_quantize: blocks of 32 along the last dim; codes [R x C(/2)], scales [R x C/32]"""
+    _check_bf16_2d(x)
+    f = _fmt(fmt)
+    rows, cols = x.shape
+    codes, scales = _outputs(x.device, rows, cols, f, out)
+    _check(lib().mx_quantize(_ptr(x), rows, cols, _ldx(x), f, _ptr(codes), _ptr(scales),
+                             _stream(x.device, stream)))
+    return codes, scales
+
+
+def quantize_transpose(x: torch.Tensor, fmt, out=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mx_quantize_transpose: blocks of 32 along dim 0; codes [C x R(/2)], scales [C x R/32]"""
+    _check_bf16_2d(x)
+    f = _fmt(fmt)
+    rows, cols = x.shape
+    codes, scales = _outputs(x.device, cols, rows, f, out)
+    _check(lib().mx_quantize_transpose(_ptr(x), rows, cols, _ldx(x), f, _ptr(codes), _ptr(scales),
+                                       _stream(x.device, stream)))
+    return codes, scales
+
+
+def hadamard32_quantize(x: torch.Tensor, fmt, sign_mask: int = 0, out=None,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mx_hadamard32_quantize: rotate each 32-row block, then transposed-mode quantize"""
+    _check_bf16_2d(x)
+    f = _fmt(fmt)
+    rows, cols = x.shape
+    codes, scales = _outputs(x.device, cols, rows, f, out)
+    _check(lib().mx_hadamard32_quantize(_ptr(x), rows, cols, _ldx(x), sign_mask & 0xFFFFFFFF, f,
+                                        _ptr(codes), _ptr(scales), _stream(x.device, stream)))
+    return codes, scales
+
+
+def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, fa, b_codes: torch.Tensor,
+         b_scales: torch.Tensor, fb, out_dtype: torch.dtype = torch.bfloat16,
+         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mx_gemm: C[M x N] = A[M x K] . B[N x K]^T on MX operands"""
+    fa_, fb_ = _fmt(fa), _fmt(fb)
+    M, kb = a_scales.shape
+    N, kb2 = b_scales.shape
+    K = 32 * kb
+    if kb2 != kb:
+        raise ValueError("A and B disagree on K")
+    for t, shp in ((a_codes, (M, code_cols(K, fa_))), (b_codes, (N, code_cols(K, fb_))),
+                   (a_scales, (M, kb)), (b_scales, (N, kb))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shp or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("operand must be contiguous uint8 of shape %s on a GPU" % (shp,))
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError("bad output buffer")
+    ldc = out.stride(0) if M > 1 else N
+    _check(lib().mx_gemm(_ptr(a_codes), _ptr(a_scales), fa_, _ptr(b_codes), _ptr(b_scales), fb_,
+                         M, N, K, _ptr(out), OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, ldc,
+                         _stream(a_codes.device, stream)))
+    return out

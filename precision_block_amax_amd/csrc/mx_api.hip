@@ -1,0 +1,141 @@
+// mx_api.hip -- the extern "C" entry points declared in include/mx.h.
+//
+// Every argument is validated on the host before the first HIP call, so the
+// error paths run (and are tested) without a GPU.  After validation the
+// current device is checked to be gfx950 (once per device, cached) and the
+// kernels are launched on the caller's stream.  Nothing is allocated and no
+// call synchronizes.
+#include <atomic>
+#include <string.h>
+
+#include "mx.h"
+#include "mx_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool fmt_ok(int f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; }
+
+int64_t code_bytes(int64_t n, int fmt) { return fmt == MX_E2M1 ? n / 2 : n; }
+
+// half-open byte ranges [p, p + n) overlap
+bool overlap(const void *p, int64_t n, const void *q, int64_t m) {
+    if (n <= 0 || m <= 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+mx_status_t check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MX_ERR_HIP;
+    if (dev >= kMaxDevices) return MX_ERR_UNSUPPORTED;
+    int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MX_ERR_HIP;
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? MX_OK : MX_ERR_UNSUPPORTED;
+}
+
+// shared checks of the three quantizers; `blocked` is the dimension cut into
+// 32-element blocks (cols in row mode, rows in transposed mode)
+mx_status_t check_quant(const void *x, int64_t rows, int64_t cols, int64_t ldx, int fmt, const void *codes,
+                        const void *scales, bool transposed) {
+    if (rows < 0 || cols < 0 || !fmt_ok(fmt)) return MX_ERR_INVALID_ARG;
+    const int64_t blocked = transposed ? rows : cols;
+    if (blocked % 32 != 0) return MX_ERR_INVALID_ARG;
+    if (ldx < cols) return MX_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return MX_OK;
+    if (!x || !codes || !scales) return MX_ERR_INVALID_ARG;
+    // index ranges the kernels address in 32 bits: octets (row mode), rows, columns
+    if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31) return MX_ERR_UNSUPPORTED;
+    if (rows > INT64_MAX / ldx) return MX_ERR_INVALID_ARG;
+    const int64_t n = rows * cols;
+    if (!transposed && n / 8 >= ((int64_t)1 << 32)) return MX_ERR_UNSUPPORTED;
+    const int64_t xb = ((rows - 1) * ldx + cols) * 2;
+    const int64_t cb = code_bytes(n, fmt), sb = n / 32;
+    if (overlap(x, xb, codes, cb) || overlap(x, xb, scales, sb) || overlap(codes, cb, scales, sb))
+        return MX_ERR_INVALID_ARG;
+    return MX_OK;
+}
+
+mx_status_t launched(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mx_status_string(mx_status_t s) {
+    switch (s) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_INVALID_ARG: return "MX_ERR_INVALID_ARG";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+    case MX_ERR_HIP: return "MX_ERR_HIP";
+    }
+    return "MX_ERR_UNKNOWN";
+}
+
+int mx_version(void) { return 100; }
+
+mx_status_t mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt,
+                        void *codes, void *scales, void *stream) {
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt, codes, scales, false);
+    if (st != MX_OK || rows == 0 || cols == 0) return st;
+    if ((st = check_device()) != MX_OK) return st;
+    return launched(mx::launch_quantize_rows((const uint16_t *)x_bf16, rows, cols, ldx, fmt, (uint8_t *)codes,
+                                             (uint8_t *)scales, (hipStream_t)stream));
+}
+
+mx_status_t mx_quantize_transpose(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                                  mx_format_t fmt, void *codes, void *scales, void *stream) {
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt, codes, scales, true);
+    if (st != MX_OK || rows == 0 || cols == 0) return st;
+    if ((st = check_device()) != MX_OK) return st;
+    return launched(mx::launch_quantize_transpose((const uint16_t *)x_bf16, rows, cols, ldx, fmt, false, 0,
+                                                  (uint8_t *)codes, (uint8_t *)scales, (hipStream_t)stream));
+}
+
+mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                                   uint32_t sign_mask, mx_format_t fmt, void *codes, void *scales,
+                                   void *stream) {
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt, codes, scales, true);
+    if (st != MX_OK || rows == 0 || cols == 0) return st;
+    if ((st = check_device()) != MX_OK) return st;
+    return launched(mx::launch_quantize_transpose((const uint16_t *)x_bf16, rows, cols, ldx, fmt, true,
+                                                  sign_mask, (uint8_t *)codes, (uint8_t *)scales,
+                                                  (hipStream_t)stream));
+}
+
+mx_status_t mx_gemm(const void *a_codes, const void *a_scales, mx_format_t fa, const void *b_codes,
+                    const void *b_scales, mx_format_t fb, int64_t M, int64_t N, int64_t K, void *c,
+                    mx_out_t out, int64_t ldc, void *stream) {
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MX_ERR_INVALID_ARG;
+    if (!fmt_ok(fa) || !fmt_ok(fb) || (out != MX_OUT_F32 && out != MX_OUT_BF16)) return MX_ERR_INVALID_ARG;
+    if (ldc < N) return MX_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MX_OK;
+    if (!c) return MX_ERR_INVALID_ARG;
+    if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return MX_ERR_INVALID_ARG;
+    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
+        return MX_ERR_UNSUPPORTED;
+    if ((M + 255) / 256 * ((N + 255) / 256) >= ((int64_t)1 << 31)) return MX_ERR_UNSUPPORTED;
+    if (M - 1 > (INT64_MAX - N) / ldc) return MX_ERR_INVALID_ARG;
+    const int64_t cbytes = ((M - 1) * ldc + N) * (out == MX_OUT_BF16 ? 2 : 4);
+    if (K > 0) {
+        const int64_t ab = M * code_bytes(K, fa), bb = N * code_bytes(K, fb);
+        const int64_t asb = M * (K / 32), bsb = N * (K / 32);
+        if (overlap(c, cbytes, a_codes, ab) || overlap(c, cbytes, a_scales, asb) ||
+            overlap(c, cbytes, b_codes, bb) || overlap(c, cbytes, b_scales, bsb))
+            return MX_ERR_INVALID_ARG;
+    }
+    mx_status_t st = check_device();
+    if (st != MX_OK) return st;
+    return launched(mx::launch_gemm((const uint8_t *)a_codes, (const uint8_t *)a_scales, fa,
+                                    (const uint8_t *)b_codes, (const uint8_t *)b_scales, fb, M, N, K, c,
+                                    out == MX_OUT_BF16, ldc, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// mx_internal.h -- launchers and small device utilities shared by the libmx
+// translation units.  Not part of the public ABI (include/mx.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx_convert.h"
+
+namespace mx {
+
+// Unsigned 32-bit division by a runtime-constant divisor d >= 1 as a
+// multiply-high and shift (Granlund & Montgomery, "Division by invariant
+// integers using multiplication", PLDI 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l for every
+// 32-bit n (the add is done in 64 bits).
+struct FastDiv {
+    uint32_t d, m, l;
+    FastDiv() : d(1), m(1), l(0) {}
+    explicit FastDiv(uint32_t div) : d(div) {
+        l = 0;
+        while ((1ull << l) < div) l++;
+        m = (uint32_t)((((1ull << l) - div) << 32) / div + 1);
+    }
+    MXHD uint32_t div(uint32_t n) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        uint32_t hi = __umulhi(m, n);
+#else
+        uint32_t hi = (uint32_t)(((uint64_t)m * n) >> 32);
+#endif
+        return (uint32_t)(((uint64_t)hi + n) >> l);
+    }
+};
+
+// Quantize launchers (mx_quant.hip).  All sizes validated by the caller;
+// they return the launch status.
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                uint8_t *codes, uint8_t *scales, hipStream_t stream);
+hipError_t launch_quantize_transpose(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                                     int fmt, bool rotate, uint32_t sign_mask, uint8_t *codes,
+                                     uint8_t *scales, hipStream_t stream);
+
+// GEMM launcher (mx_gemm.hip).
+hipError_t launch_gemm(const uint8_t *a, const uint8_t *as, int fa, const uint8_t *b,
+                       const uint8_t *bs, int fb, int64_t M, int64_t N, int64_t K, void *c,
+                       bool bf16_out, int64_t ldc, hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,321 @@
+// mx_quant.hip -- MX quantizers for gfx950: row mode, transposed mode, and
+// transposed mode after the fixed-sign 32-point block-Hadamard rotation.
+//
+// Method: MX micro-scaling, block 32 along the reduction dimension, E8M0
+// scale from the block amax, round-to-nearest-even saturating element casts
+// (FP4-training article on hzrcw.cc, section 02; MindSpeed-LLM FSDP2 page,
+// recipe dynamic_MX-1-1-32); the rotation is the deterministic Hadamard
+// transform that article applies on the weight-gradient path.  Element and
+// scale arithmetic is in mx_convert.h.
+//
+// All three kernels are HBM-bandwidth bound (2 B read + 1 or 0.5 B written +
+// 1/32 B of scale per element).  Design:
+//   row mode   each lane holds 8 consecutive bf16 (one 16-byte load), four
+//              neighbouring lanes form a 32-element block, the block amax is a
+//              two-step DPP quad reduction; every load and store instruction
+//              of a wave covers one contiguous span.
+//   transposed each lane holds 4 adjacent columns of a 32-row block (32
+//              8-byte loads, each wave instruction reading 512 contiguous
+//              bytes of one row), so a whole block sits in one lane's
+//              registers: amax and, for the rotation, the five butterfly
+//              stages need no cross-lane traffic and no LDS.  The four waves
+//              of a workgroup take four consecutive row blocks, so each output
+//              row receives 128 contiguous code bytes (FP8) from one workgroup.
+#include "mx_internal.h"
+
+namespace mx {
+namespace {
+
+constexpr uint32_t kRowThreads = 256;
+constexpr uint32_t kRowUnroll = 4;  // 16-byte loads in flight per lane
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// max over the four lanes of a DPP quad (lanes 4q .. 4q+3)
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));  // lane ^ 2
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Row mode.  Octet o covers elements 8o .. 8o+7 of the row-major [rows x cols]
+// view; cols % 32 == 0 keeps every block inside one quad of lanes.
+template <int F, bool CONTIG, bool VEC>
+__global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
+    const uint16_t *__restrict__ x, int64_t ldx, uint32_t total_oct, uint32_t oct_per_row,
+    FastDiv row_div, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    const uint32_t o0 = blockIdx.x * (kRowThreads * kRowUnroll) + threadIdx.x;
+    uint32_t w[kRowUnroll][4];
+
+#pragma unroll
+    for (uint32_t u = 0; u < kRowUnroll; u++) {
+        const uint32_t o = o0 + u * kRowThreads;
+        w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0;
+        if (o < total_oct) {
+            const uint16_t *p;
+            if (CONTIG) {
+                p = x + (uint64_t)o * 8;
+            } else {
+                const uint32_t r = row_div.div(o);
+                p = x + (int64_t)r * ldx + (uint64_t)(o - r * oct_per_row) * 8;
+            }
+            if (VEC) {
+                const uint4 t = *reinterpret_cast<const uint4 *>(p);
+                w[u][0] = t.x; w[u][1] = t.y; w[u][2] = t.z; w[u][3] = t.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++) w[u][i] = (uint32_t)p[2 * i] | ((uint32_t)p[2 * i + 1] << 16);
+            }
+        }
+    }
+
+#pragma unroll
+    for (uint32_t u = 0; u < kRowUnroll; u++) {
+        const uint32_t o = o0 + u * kRowThreads;
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t a = w[u][i] & 0x7FFF7FFFu;
+            m = umax(m, umax(a & 0xFFFFu, a >> 16));
+        }
+        m = quad_max(m);  // every lane runs the exchange; out-of-range quads hold zeros
+        const bool finite = m < 0x7F80u;
+        const int e = scale_exp_bf16<F>(finite ? m : 0u);
+        uint32_t c[8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            c[2 * i] = finite ? code_from_bf16<F>(w[u][i] & 0xFFFFu, e) : 0u;
+            c[2 * i + 1] = finite ? code_from_bf16<F>(w[u][i] >> 16, e) : 0u;
+        }
+        if (o < total_oct) {
+            if (F == E2M1) {
+                uint32_t packed = 0;
+#pragma unroll
+                for (int i = 0; i < 8; i++) packed |= c[i] << (4 * i);
+                if (VEC) {
+                    *reinterpret_cast<uint32_t *>(codes + (uint64_t)o * 4) = packed;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) codes[(uint64_t)o * 4 + i] = (uint8_t)(packed >> (8 * i));
+                }
+            } else {
+                const uint32_t lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+                const uint32_t hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+                if (VEC) {
+                    *reinterpret_cast<uint2 *>(codes + (uint64_t)o * 8) = make_uint2(lo, hi);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        codes[(uint64_t)o * 8 + i] = (uint8_t)(lo >> (8 * i));
+                        codes[(uint64_t)o * 8 + 4 + i] = (uint8_t)(hi >> (8 * i));
+                    }
+                }
+            }
+            if ((threadIdx.x & 3u) == 0) scales[o >> 2] = (uint8_t)(finite ? e + 127 : 0xFF);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed mode, optionally after the rotation.  Lane: 4 columns
+// c0 .. c0+3; wave: row block rb (32 rows); workgroup: 4 row blocks x 256
+// columns.
+constexpr int kTrColsPerLane = 4;
+constexpr int kTrWaves = 4;
+
+// y = c * H32 * diag(s) * x, stages h = 1, 2, 4, 8, 16, one fp32 rounding per op
+__device__ __forceinline__ void hadamard32(float (&y)[32], uint32_t sign_mask) {
+    if (sign_mask) {
+#pragma unroll
+        for (int i = 0; i < 32; i++) y[i] = __uint_as_float(__float_as_uint(y[i]) ^ (((sign_mask >> i) & 1u) << 31));
+    }
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            if (!(j & h)) {
+                const float a = y[j], b = y[j + h];
+                y[j] = __fadd_rn(a, b);
+                y[j + h] = __fsub_rn(a, b);
+            }
+        }
+    }
+    const float c = __uint_as_float(0x3E3504F3u);  // RN_fp32(1/sqrt(32))
+#pragma unroll
+    for (int i = 0; i < 32; i++) y[i] = __fmul_rn(y[i], c);
+}
+
+template <int F>
+__device__ __forceinline__ void store_block_codes(uint8_t *dst, const uint32_t (&c)[32], bool vec) {
+    if (F == E2M1) {
+        uint32_t p[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            p[q] = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) p[q] |= c[8 * q + i] << (4 * i);
+        }
+        if (vec) {
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) dst[i] = (uint8_t)(p[i >> 2] >> (8 * (i & 3)));
+        }
+    } else {
+        uint32_t p[8];
+#pragma unroll
+        for (int q = 0; q < 8; q++) p[q] = c[4 * q] | (c[4 * q + 1] << 8) | (c[4 * q + 2] << 16) | (c[4 * q + 3] << 24);
+        if (vec) {
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
+            *reinterpret_cast<uint4 *>(dst + 16) = make_uint4(p[4], p[5], p[6], p[7]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; i++) dst[i] = (uint8_t)(p[i >> 2] >> (8 * (i & 3)));
+        }
+    }
+}
+
+template <int F, bool ROTATE, bool VEC>
+__global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
+    const uint16_t *__restrict__ x, int64_t ldx, int64_t rows, int64_t cols, uint32_t sign_mask,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * kTrColsPerLane;
+    const int64_t rb = (int64_t)blockIdx.y * kTrWaves + wave;
+    const int64_t nrb = rows / 32;
+    if (rb >= nrb || c0 >= cols) return;  // no barriers or cross-lane ops below
+    const int ncols = (int)((cols - c0) < kTrColsPerLane ? (cols - c0) : kTrColsPerLane);
+
+    // w[i][0] = columns c0, c0+1 of row 32 rb + i; w[i][1] = columns c0+2, c0+3
+    uint32_t w[32][2];
+    const uint16_t *p = x + rb * 32 * ldx + c0;
+    if (VEC && ncols == kTrColsPerLane) {
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            const uint2 t = *reinterpret_cast<const uint2 *>(p + i * ldx);
+            w[i][0] = t.x;
+            w[i][1] = t.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            uint32_t v[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) v[j] = j < ncols ? p[i * ldx + j] : 0u;
+            w[i][0] = v[0] | (v[1] << 16);
+            w[i][1] = v[2] | (v[3] << 16);
+        }
+    }
+
+    const int64_t row_bytes = (F == E2M1) ? rows / 2 : rows;
+#pragma unroll
+    for (int j = 0; j < kTrColsPerLane; j++) {
+        if (j >= ncols) break;
+        uint32_t c[32];
+        int S;
+        if (ROTATE) {
+            float y[32];
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                const uint32_t d = w[i][j >> 1];
+                y[i] = __uint_as_float((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
+            }
+            hadamard32(y, sign_mask);
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 32; i++) m = umax(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+            const bool finite = m < 0x7F800000u;
+            const int e = scale_exp_f32<F>(finite ? m : 0u);
+#pragma unroll
+            for (int i = 0; i < 32; i++) c[i] = finite ? code_from_f32<F>(y[i], e) : 0u;
+            S = finite ? e + 127 : 0xFF;
+        } else {
+            uint32_t b[32];
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                const uint32_t d = w[i][j >> 1];
+                b[i] = (j & 1) ? (d >> 16) : (d & 0xFFFFu);
+                m = umax(m, b[i] & 0x7FFFu);
+            }
+            const bool finite = m < 0x7F80u;
+            const int e = scale_exp_bf16<F>(finite ? m : 0u);
+#pragma unroll
+            for (int i = 0; i < 32; i++) c[i] = finite ? code_from_bf16<F>(b[i], e) : 0u;
+            S = finite ? e + 127 : 0xFF;
+        }
+        const int64_t col = c0 + j;
+        store_block_codes<F>(codes + col * row_bytes + rb * (F == E2M1 ? 16 : 32), c, VEC);
+        scales[col * nrb + rb] = (uint8_t)S;
+    }
+}
+
+template <int F>
+hipError_t launch_rows_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint8_t *codes,
+                           uint8_t *scales, hipStream_t stream) {
+    const uint64_t total = (uint64_t)rows * (uint64_t)cols / 8;
+    const uint32_t opr = (uint32_t)(cols / 8);
+    const bool contig = ldx == cols;
+    const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0) &&
+                     ((uintptr_t)codes % (F == E2M1 ? 4 : 8) == 0);
+    const uint32_t per_block = kRowThreads * kRowUnroll;
+    const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+    const FastDiv div(opr);
+    if (contig && vec)
+        hipLaunchKernelGGL((k_quantize_rows<F, true, true>), grid, dim3(kRowThreads), 0, stream, x, ldx,
+                           (uint32_t)total, opr, div, codes, scales);
+    else if (vec)
+        hipLaunchKernelGGL((k_quantize_rows<F, false, true>), grid, dim3(kRowThreads), 0, stream, x, ldx,
+                           (uint32_t)total, opr, div, codes, scales);
+    else
+        hipLaunchKernelGGL((k_quantize_rows<F, false, false>), grid, dim3(kRowThreads), 0, stream, x, ldx,
+                           (uint32_t)total, opr, div, codes, scales);
+    return hipGetLastError();
+}
+
+template <int F, bool ROTATE>
+hipError_t launch_tr_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint32_t mask,
+                         uint8_t *codes, uint8_t *scales, hipStream_t stream) {
+    const bool vec = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0) && ((uintptr_t)codes % 16 == 0);
+    const dim3 grid((unsigned)((cols + 64 * kTrColsPerLane - 1) / (64 * kTrColsPerLane)),
+                    (unsigned)((rows / 32 + kTrWaves - 1) / kTrWaves));
+    if (vec)
+        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true>), grid, dim3(64 * kTrWaves), 0, stream, x, ldx,
+                           rows, cols, mask, codes, scales);
+    else
+        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, false>), grid, dim3(64 * kTrWaves), 0, stream, x,
+                           ldx, rows, cols, mask, codes, scales);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                uint8_t *codes, uint8_t *scales, hipStream_t stream) {
+    switch (fmt) {
+    case E4M3: return launch_rows_fmt<E4M3>(x, rows, cols, ldx, codes, scales, stream);
+    case E5M2: return launch_rows_fmt<E5M2>(x, rows, cols, ldx, codes, scales, stream);
+    default: return launch_rows_fmt<E2M1>(x, rows, cols, ldx, codes, scales, stream);
+    }
+}
+
+hipError_t launch_quantize_transpose(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                                     int fmt, bool rotate, uint32_t sign_mask, uint8_t *codes,
+                                     uint8_t *scales, hipStream_t stream) {
+    if (rotate) {
+        switch (fmt) {
+        case E4M3: return launch_tr_fmt<E4M3, true>(x, rows, cols, ldx, sign_mask, codes, scales, stream);
+        case E5M2: return launch_tr_fmt<E5M2, true>(x, rows, cols, ldx, sign_mask, codes, scales, stream);
+        default: return launch_tr_fmt<E2M1, true>(x, rows, cols, ldx, sign_mask, codes, scales, stream);
+        }
+    }
+    switch (fmt) {
+    case E4M3: return launch_tr_fmt<E4M3, false>(x, rows, cols, ldx, 0, codes, scales, stream);
+    case E5M2: return launch_tr_fmt<E5M2, false>(x, rows, cols, ldx, 0, codes, scales, stream);
+    default: return launch_tr_fmt<E2M1, false>(x, rows, cols, ldx, 0, codes, scales, stream);
+    }
+}
+
+}  // namespace mx

@@ -1,0 +1,164 @@
+"""GPU parity of mx_gemm against the oracle, within the fp32 accumulation tolerance.
+
+|C_gpu - C_ref| <= 1e-5 * sum_k |a_mk b_nk| per element (plus half a bf16 ulp
+when the output is bf16); elements with S_abs = 0 must be exactly 0.  The
+operands come from the oracle's own quantization of the seeded inputs, so the
+GEMM is checked in isolation; the end-to-end chain (GPU quantizers feeding the
+GPU GEMM) is checked too, bit-exact codes being established by the quantizer
+tests.  Full-size configurations are compared on sampled rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import check_gemm, to_dev_bf16, to_dev_u8, to_host
+
+pytestmark = pytest.mark.gpu
+FMTS = ("e4m3", "e5m2", "e2m1")
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import precision_block_amax_amd as m
+    m.lib()
+    return m
+
+
+def _run(mx, qa, fa, qb, fb, bf16, out=None):
+    import torch
+    return mx.gemm(to_dev_u8(qa[0]), to_dev_u8(qa[1]), fa, to_dev_u8(qb[0]), to_dev_u8(qb[1]), fb,
+                   out_dtype=torch.bfloat16 if bf16 else torch.float32, out=out)
+
+
+def _host_c(c, bf16):
+    h = to_host(c)
+    return workloads.bf16_bits_to_f32(h).astype(np.float64) if bf16 else h.astype(np.float64)
+
+
+def _oracle_operands(cfg, qname):
+    q = cfg.quant(qname)
+    x = workloads.draw_tensor(cfg, q.tensor)
+    if q.kind == "row":
+        return oracle.quantize(x, q.fmt)
+    if q.kind == "transpose":
+        return oracle.quantize_transpose(x, q.fmt)
+    return oracle.hadamard32_quantize(x, q.fmt, q.sign_mask)
+
+
+def test_small_config_all_elements(mx):
+    cfg = workloads.config(0)
+    g = cfg.gemms[0]
+    qa, qb = _oracle_operands(cfg, g.a), _oracle_operands(cfg, g.b)
+    C, S = oracle.gemm(qa[0], qa[1], "e4m3", qb[0], qb[1], "e4m3")
+    c = _run(mx, qa, "e4m3", qb, "e4m3", False)
+    r = check_gemm(_host_c(c, False), C, S, False)
+    print("max |err|/S", r)
+
+
+def test_small_config_end_to_end(mx):
+    """GPU quantizers feeding the GPU GEMM: codes equal the oracle's, C within tolerance"""
+    import torch
+    cfg = workloads.config(0)
+    a = workloads.draw_tensor(cfg, "A")
+    b = workloads.draw_tensor(cfg, "B")
+    ca, sa = mx.quantize(to_dev_bf16(a), "e4m3")
+    cb, sb = mx.quantize_transpose(to_dev_bf16(b), "e4m3")
+    c = mx.gemm(ca, sa, "e4m3", cb, sb, "e4m3", out_dtype=torch.float32)
+    qa, qb = oracle.quantize(a, "e4m3"), oracle.quantize_transpose(b, "e4m3")
+    assert np.array_equal(to_host(ca), qa[0]) and np.array_equal(to_host(sb), qb[1])
+    C, S = oracle.gemm(qa[0], qa[1], "e4m3", qb[0], qb[1], "e4m3")
+    check_gemm(_host_c(c, False), C, S, False)
+
+
+@pytest.mark.parametrize("fa,fb,a,b,want", [("e4m3", "e4m3", 1.0, 1.0, 32.0), ("e2m1", "e2m1", 6.0, -0.5, -96.0)])
+def test_worked_examples(mx, fa, fb, a, b, want):
+    import torch
+    xa = torch.full((1, 32), a, dtype=torch.bfloat16, device="cuda")
+    xb = torch.full((1, 32), b, dtype=torch.bfloat16, device="cuda")
+    ca, sa = mx.quantize(xa, fa)
+    cb, sb = mx.quantize(xb, fb)
+    c = mx.gemm(ca, sa, fa, cb, sb, fb, out_dtype=torch.float32)
+    assert to_host(c)[0, 0] == want
+
+
+def _rand_operand(rng, rows, K, fmt):
+    import torch
+    v = (rng.standard_t(4, (rows, K)) * np.exp2(rng.integers(-6, 6, (rows, K // 32))).repeat(32, 1)).astype(np.float32)
+    bits = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return oracle.quantize(bits, fmt)
+
+
+@pytest.mark.parametrize("fa", FMTS)
+@pytest.mark.parametrize("fb", FMTS)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_format_pairs_with_tails(mx, fa, fb, bf16):
+    """every format pair; M, N not multiples of the tile; K not a multiple of the K tile"""
+    rng = np.random.default_rng(FMTS.index(fa) * 3 + FMTS.index(fb))
+    M, N, K = 300, 200, 352
+    qa, qb = _rand_operand(rng, M, K, fa), _rand_operand(rng, N, K, fb)
+    C, S = oracle.gemm(qa[0], qa[1], fa, qb[0], qb[1], fb)
+    check_gemm(_host_c(_run(mx, qa, fa, qb, fb, bf16), bf16), C, S, bf16)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (33, 17, 64), (256, 512, 32), (512, 256, 1024), (64, 1000, 160)])
+def test_shapes(mx, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    qa, qb = _rand_operand(rng, M, K, "e4m3"), _rand_operand(rng, N, K, "e2m1")
+    C, S = oracle.gemm(qa[0], qa[1], "e4m3", qb[0], qb[1], "e2m1")
+    check_gemm(_host_c(_run(mx, qa, "e4m3", qb, "e2m1", False), False), C, S, False)
+
+
+def test_ldc_and_zero_k(mx):
+    import torch
+    rng = np.random.default_rng(3)
+    qa, qb = _rand_operand(rng, 70, 128, "e5m2"), _rand_operand(rng, 90, 128, "e4m3")
+    C, S = oracle.gemm(qa[0], qa[1], "e5m2", qb[0], qb[1], "e4m3")
+    big = torch.full((70, 128), 7.0, dtype=torch.float32, device="cuda")
+    out = big[:, 10:100]
+    _run(mx, qa, "e5m2", qb, "e4m3", False, out=out)
+    h = to_host(big)
+    check_gemm(h[:, 10:100].astype(np.float64), C, S, False)
+    assert np.all(h[:, :10] == 7.0) and np.all(h[:, 100:] == 7.0)
+    # K = 0: C = 0
+    z = mx.gemm(torch.empty(5, 0, dtype=torch.uint8, device="cuda"), torch.empty(5, 0, dtype=torch.uint8, device="cuda"),
+                "e4m3", torch.empty(6, 0, dtype=torch.uint8, device="cuda"),
+                torch.empty(6, 0, dtype=torch.uint8, device="cuda"), "e4m3", out_dtype=torch.float32)
+    assert np.all(to_host(z) == 0)
+
+
+def test_zero_and_nan_blocks(mx):
+    """an all-zero block contributes 0; a NaN-scale block (0xFF) makes its row NaN"""
+    import torch
+    rng = np.random.default_rng(8)
+    qa, qb = _rand_operand(rng, 64, 128, "e4m3"), _rand_operand(rng, 64, 128, "e4m3")
+    qa[0][3] = 0
+    qa[1][3] = 0
+    C, S = oracle.gemm(qa[0], qa[1], "e4m3", qb[0], qb[1], "e4m3")
+    c = _host_c(_run(mx, qa, "e4m3", qb, "e4m3", False), False)
+    assert np.all(c[3] == 0)
+    check_gemm(c, C, S, False)
+    qa[1][5, 2] = 0xFF
+    c = _host_c(_run(mx, qa, "e4m3", qb, "e4m3", True), True)
+    assert np.all(np.isnan(c[5]))
+
+
+FULL = [(1, "Y", True), (2, "Y", True), (3, "dW", False)]
+
+
+@pytest.mark.parametrize("ci,gname,bf16", FULL)
+def test_full_size_sampled_rows(mx, ci, gname, bf16):
+    """full-size GEMM launched as the benchmark launches it; oracle on sampled rows"""
+    cfg = workloads.config(ci)
+    g = [x for x in cfg.gemms if x.name == gname][0]
+    print("case", cfg.name, g.name, g.M, g.N, g.K, flush=True)
+    qa_spec, qb_spec = cfg.quant(g.a), cfg.quant(g.b)
+    qa, qb = _oracle_operands(cfg, g.a), _oracle_operands(cfg, g.b)
+    c = _host_c(_run(mx, qa, qa_spec.fmt, qb, qb_spec.fmt, bf16), bf16)
+    rng = np.random.default_rng(ci)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, g.M - 1], rng.integers(0, g.M, 59)]))
+    C, S = oracle.gemm(qa[0], qa[1], qa_spec.fmt, qb[0], qb[1], qb_spec.fmt, rows=rows)
+    r = check_gemm(c[rows], C, S, bf16)
+    print("max |err|/S", r, flush=True)
