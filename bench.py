@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the MX quantize / block-Hadamard / MX-GEMM hot path on one MI355X.
+
+One step runs the three Llama-3.1-8B linear-layer workloads back to back on
+seeded synthetic inputs already resident in device memory:
+  QKV Fprop, MXFP8:     quantize X [8192x4096] and W [6144x4096] to E4M3,
+                        Y[8192x6144] = X W^T, bf16 out;
+  gate+up Fprop, MXFP4: quantize X [8192x4096] and W [28672x4096] to E2M1,
+                        Y[8192x28672] = X W^T, bf16 out;
+  down-proj Wgrad, MXFP4 with the fixed block-Hadamard rotation:
+                        rotate-and-transpose-quantize dY [8192x14336] and
+                        X [8192x4096] along tokens to E2M1,
+                        dW[14336x4096] = dY^T X, fp32 out.
+The pages quote their gains on Llama-3.1-8B pre-training on MI355X
+(FP4-training article on hzrcw.cc, section 03); these are that model's
+linear-layer shapes.  `value` is the step's GEMM work divided by the whole
+step time (quantizers included), in TFLOP/s.  Each kernel is also timed with
+HIP events on the stream it runs on and reported against its roofline.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+# MI355X published peaks (dense)
+PEAK_HBM_GBPS = 8000.0
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+CONFIGS = (1, 2, 3)  # the three Llama-3.1-8B workloads
+WORKLOAD = "llama31_8b_linear_set"
+
+
+def quant_bytes(rows: int, cols: int, fmt: str) -> float:
+    """algorithmic HBM bytes of one quantize call: bf16 in, codes + scales out"""
+    return rows * cols * (2.0 + (0.5 if fmt == "e2m1" else 1.0) + 1.0 / 32)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "precision_block_amax_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None"""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_sha") != kernel_source_sha():
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+class Step:
+    """device buffers and the ordered kernel launches of one step"""
+
+    def __init__(self, mx, torch, seed: int):
+        self.mx, self.torch = mx, torch
+        self.launches = []  # (name, kind, work, fn)
+        dev = torch.device("cuda", 0)
+
+        def bf16(cfg, name):
+            bits = workloads.draw_tensor(cfg, name, seed=seed)
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        for ci in CONFIGS:
+            cfg = workloads.config(ci)
+            tens = {t.name: bf16(cfg, t.name) for t in cfg.tensors}
+            ops = {}
+            for q in cfg.quants:
+                x = tens[q.tensor]
+                rows, cols = x.shape
+                out_rows, k = (rows, cols) if q.kind == "row" else (cols, rows)
+                codes = torch.empty((out_rows, mx.code_cols(k, q.fmt)), dtype=torch.uint8, device=dev)
+                scales = torch.empty((out_rows, k // 32), dtype=torch.uint8, device=dev)
+                ops[q.name] = (codes, scales, q.fmt)
+                fn = {"row": lambda x=x, q=q, c=codes, s=scales: mx.quantize(x, q.fmt, out=(c, s)),
+                      "transpose": lambda x=x, q=q, c=codes, s=scales: mx.quantize_transpose(x, q.fmt, out=(c, s)),
+                      "hadamard": lambda x=x, q=q, c=codes, s=scales: mx.hadamard32_quantize(
+                          x, q.fmt, q.sign_mask, out=(c, s))}[q.kind]
+                kname = {"row": "mx_quantize", "transpose": "mx_quantize_transpose",
+                         "hadamard": "mx_hadamard32_quantize"}[q.kind]
+                self.launches.append(("%s/%s %s %s" % (cfg.name, q.name, kname, q.fmt), "quant",
+                                      quant_bytes(rows, cols, q.fmt), fn))
+            for gm in cfg.gemms:
+                a, b = ops[gm.a], ops[gm.b]
+                out = torch.empty((gm.M, gm.N), dtype=torch.bfloat16 if gm.out == "bf16" else torch.float32,
+                                  device=dev)
+                fn = (lambda a=a, b=b, out=out: mx.gemm(a[0], a[1], a[2], b[0], b[1], b[2],
+                                                        out_dtype=out.dtype, out=out))
+                arith = "fp4" if a[2] == "e2m1" and b[2] == "e2m1" else "bf16"
+                self.launches.append(("%s/%s mx_gemm %sx%s" % (cfg.name, gm.name, a[2], b[2]), "gemm:" + arith,
+                                      2.0 * gm.M * gm.N * gm.K, fn))
+        self.flops = sum(w for _, kind, w, _ in self.launches if kind.startswith("gemm"))
+
+    def run(self, events=None):
+        for i, (_, _, _, fn) in enumerate(self.launches):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+
+def cpu_baseline(seed: int, step_flops: float) -> dict:
+    """the oracle on a bounded sample of the same step, extrapolated to the
+    step; rows per quantize and rows of A per GEMM are sampled"""
+    import oracle
+    qrows, grow_a, grow_b = 512, 8, 40
+    t_total = 0.0
+    parts = []
+    for ci in CONFIGS:
+        cfg = workloads.config(ci)
+        ops = {}
+        for q in cfg.quants:
+            spec = cfg.tensor(q.tensor)
+            x = workloads.draw_tensor(cfg, q.tensor, seed=seed, rows=(0, qrows))
+            fn = {"row": lambda: oracle.quantize(x, q.fmt),
+                  "transpose": lambda: oracle.quantize_transpose(x, q.fmt),
+                  "hadamard": lambda: oracle.hadamard32_quantize(x, q.fmt, q.sign_mask)}[q.kind]
+            t0 = time.perf_counter()
+            fn()
+            dt = time.perf_counter() - t0
+            t_total += dt * spec.rows / qrows
+            parts.append("%s/%s: %d of %d rows" % (cfg.name, q.name, qrows, spec.rows))
+        for gm in cfg.gemms:
+            qa, qb = cfg.quant(gm.a), cfg.quant(gm.b)
+            # operands from the oracle's own quantizers (full tensors: the GEMM needs all of B)
+            def operand(q):
+                x = workloads.draw_tensor(cfg, q.tensor, seed=seed)
+                if q.kind == "row":
+                    return oracle.quantize(x, q.fmt)
+                if q.kind == "transpose":
+                    return oracle.quantize_transpose(x, q.fmt)
+                return oracle.hadamard32_quantize(x, q.fmt, q.sign_mask)
+            A, B = operand(qa), operand(qb)
+            times = []
+            for r in (grow_a, grow_b):
+                t0 = time.perf_counter()
+                oracle.gemm(A[0], A[1], qa.fmt, B[0], B[1], qb.fmt, rows=np.arange(r))
+                times.append(time.perf_counter() - t0)
+            per_row = max(times[1] - times[0], 0.0) / (grow_b - grow_a)
+            fixed = max(times[0] - per_row * grow_a, 0.0)
+            t_total += fixed + per_row * gm.M
+            parts.append("%s/%s: GEMM rows %d and %d of %d, linear fit" % (cfg.name, gm.name, grow_a, grow_b, gm.M))
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return {"value": step_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "; ".join(parts) + "; per-step time extrapolated to %.1f s" % t_total}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=workloads.DEFAULT_SEED)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the hot path runs on a single MI355X and this build "
+              "has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import precision_block_amax_amd as mx
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    mx.lib()
+    torch.cuda.set_device(0)
+
+    print("bench: building inputs", file=sys.stderr, flush=True)
+    step = Step(mx, torch, args.seed)
+    torch.cuda.synchronize()
+    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    n = len(step.launches)
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(n)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step.run(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    print("bench: timed %d steps, %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
+
+    kernels = []
+    for i, (name, kind, work, _) in enumerate(step.launches):
+        ms = float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
+        if kind == "quant":
+            ach = work / (ms * 1e-3) / 1e9
+            kernels.append({"kernel": name, "ms": ms, "bound": "hbm", "achieved": ach, "unit": "GB/s",
+                            "peak": PEAK_HBM_GBPS, "frac": ach / PEAK_HBM_GBPS, "work": work})
+        else:
+            arith = kind.split(":")[1]
+            ach = work / (ms * 1e-3) / 1e12
+            k = {"kernel": name, "ms": ms, "bound": "mfma", "achieved": ach, "unit": "TFLOP/s",
+                 "peak": PEAK_TFLOPS[arith], "frac": ach / PEAK_TFLOPS[arith], "arith": arith, "work": work}
+            if arith == "bf16":  # MXFP8 operands carried as bf16: also against the MXFP8 peak
+                k["frac_of_mxfp8_peak"] = ach / PEAK_TFLOPS["fp8"]
+            kernels.append(k)
+
+    dom = max(kernels, key=lambda k: k["ms"])
+    traffic = measured_traffic(dom["kernel"])
+    roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3), "peak": dom["peak"],
+                "unit": dom["unit"], "frac": round(dom["frac"], 4), "traffic": traffic, "kernel": dom["kernel"]}
+    q = [k for k in kernels if k["bound"] == "hbm"]
+    quant_gbps = sum(k["work"] for k in q) / (sum(k["ms"] for k in q) * 1e-3) / 1e9
+
+    value = step.flops / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": "MX-GEMM TFLOPS & quantize GB/s at Llama-3.1-8B shapes, % of MI355X peak",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8/mxfp4 operands, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "global_batch": 8192, "seq_len": 8192, "parallelism": "none",
+                   "gemms": [k["kernel"] for k in kernels if k["bound"] == "mfma"]},
+        "roofline": roofline,
+        "quantize_GBps": round(quant_gbps, 1), "quantize_frac_of_hbm_peak": round(quant_gbps / PEAK_HBM_GBPS, 4),
+        "kernels": [{kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in k.items() if kk != "work"}
+                    for k in kernels],
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle on a bounded sample)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.seed, step.flops)
+    if args.kernels:
+        for k in kernels:
+            print("%-70s %8.1f us  %9.1f %s  %5.1f%%" % (k["kernel"], k["ms"] * 1e3, k["achieved"], k["unit"],
+                                                       100 * k["frac"]), file=sys.stderr)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

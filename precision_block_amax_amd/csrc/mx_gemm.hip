@@ -6,36 +6,57 @@
 // quantized training (FP4-training article on hzrcw.cc, section 02), which
 // the Primus page identifies as the dominant training cost.
 //
-// Design (MFMA-bound; 2*M*N*K flops):
-//   - V_MFMA_SCALE_F32_32X32X64_F8F6F4 (K = 64 per instruction): lane l
-//     serves row l % 32 of A (column of B); its half h = l / 32 supplies the
-//     E8M0 byte of K block h, and the matrix core applies both scales, so
-//     there is no dequantization pass.  Operand bytes per lane (measured on
-//     gfx950): FP4 -- 16 bytes = K[32h, 32h+32), one whole block; FP8 -- 32
-//     bytes = K[16h, 16h+16) followed by K[32+16h, 32+16h+16), i.e. 16-byte
-//     chunks h and 2+h of the 64-byte K step.  FP8 (E4M3 / E5M2) and FP4
-//     (E2M1) operands mix freely.
-//   - Workgroup tile 256 x 256, four waves of 128 x 128 (4 x 4 MFMA tiles,
-//     256 fp32 accumulators per lane).  K tile: 128 bytes of codes per row
-//     (128 FP8 or 256 FP4 elements).
-//   - Operand tiles are double-buffered in LDS (2 x 64 KiB) with the 16-byte
-//     chunks of each row XOR-swizzled by the row index, so the 32 lanes that
-//     read the same K chunk of 32 consecutive rows hit distinct banks.  One
-//     barrier per K tile; the next tile's global loads are in flight while
-//     the current tile is multiplied.
-//   - Scales of a K tile (4 or 8 bytes per row) are staged in LDS beside the
-//     codes; a lane selects its block's byte with the instruction's op_sel.
-//   - Tile order: workgroups are dealt round-robin to the 8 XCDs, so each XCD
-//     gets a contiguous run of tiles, ordered in groups of 8 tile rows, to keep
-//     shared A rows and B columns in that XCD's L2.
-//   - M and N tails: loads clamp to the last valid row and stores are masked;
-//     the K tail is zero-filled (code 0, scale byte 0).
+// Two kernels share one tiling (MFMA-bound; 2*M*N*K flops):
+//   - workgroup tile 256 x 256, four waves of 128 x 128 (4 x 4 tiles of
+//     32 x 32, 256 fp32 accumulators per lane);
+//   - operand codes and scales double-buffered in LDS, the 16-byte chunks of
+//     each code row XOR-swizzled by the row index so that the lanes reading
+//     one K chunk of consecutive rows hit distinct banks; one barrier per K
+//     tile, the next tile's global loads in flight during the current tile's
+//     matrix work;
+//   - workgroups are dealt round-robin to the 8 XCDs, so each XCD gets a
+//     contiguous run of tiles, ordered in groups of 8 tile rows, to keep shared
+//     A rows and B columns in that XCD's L2;
+//   - M and N tails: loads clamp to the last valid row, stores are masked; the
+//     K tail is zero-filled (code 0, scale byte 0).
+//
+// k_gemm_fp4 (E2M1 x E2M1): V_MFMA_SCALE_F32_32X32X64_F8F6F4.  Lane l serves
+// row l % 32 of A (column of B); its half h = l / 32 holds K[32h, 32h+32) of
+// the 64-element step -- one whole MX block -- and supplies that block's
+// E8M0 byte; the matrix core applies both scales.  Measured on gfx950: the
+// products of two E2M1 values span few enough binades that the instruction's
+// internal sum is exact, so only the fp32 accumulation rounds.
+//
+// k_gemm_carrier (any pair with an FP8 operand): measured on gfx950, the
+// scaled instruction sums the products of an FP8 block in a fixed-point
+// window about 13 bits below the largest product (1 + 2^-13 survives, 1 +
+// 2^-14 does not), an error of up to ~1e-4 of sum |a*b| on random codes --
+// outside the fp32 accumulation tolerance this library is held to.  So FP8
+// codes travel as bf16 (every E4M3 / E5M2 / E2M1 value times a power of two
+// in [2^-40, 1] is an exact bf16) through V_MFMA_F32_32X32X16_BF16, whose
+// 16-product sum is exact with one fp32 rounding:
+//   a'[m, k] = code * 2^(S_a[m, b] - R_a[m]),  R_a[m] = max_b S_a[m, b]
+// (V_CVT_SCALEF32_PK_BF16_{FP8,BF8,FP4}: two codes per instruction, exact for
+// normal power-of-two scales), same for B, and C = 2^(R_a + R_b - 254) *
+// sum a' b'.  A tile in which some row's scales spread over more than 40
+// binades, or which holds an E8M0 NaN (0xFF), is left to a second kernel with
+// an exact per-block path: each 32-element block's partial sum of unscaled
+// codes is scaled with ldexp and added in fp32 (separate kernels keep the
+// VALU-side accumulation out of the fast kernel's register budget).
 #include <type_traits>
 
 #include "mx_internal.h"
 
 namespace mx {
 namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int BM = 256, BN = 256, NT = 256;
+constexpr int kSpreadMax = 40;  // carrier fast path: per-row scale spread, binades
 
 // compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N)
 template <int I, int N, class Fn>
@@ -45,17 +66,6 @@ __device__ __forceinline__ void static_for(Fn &&f) {
         static_for<I + 1, N>(f);
     }
 }
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-constexpr int BM = 256, BN = 256, NT = 256;
-
-// matrix-core format selector (cbsz / blgp)
-template <int F> struct MfmaFmt;
-template <> struct MfmaFmt<E4M3> { static constexpr int v = 0; };
-template <> struct MfmaFmt<E5M2> { static constexpr int v = 1; };
-template <> struct MfmaFmt<E2M1> { static constexpr int v = 4; };
 
 struct GemmArgs {
     const uint8_t *a, *as, *b, *bs;
@@ -68,8 +78,8 @@ struct GemmArgs {
 // byte offset of 16-byte chunk `ch` of row `row` in a swizzled LDS tile
 template <int RB>
 __device__ __forceinline__ int swz(int row, int ch) {
-    if (RB == 128) return row * 128 + ((ch ^ (row & 7)) << 4);
-    return row * 64 + ((ch ^ ((row >> 1) & 3)) << 4);  // 64-byte rows: two rows per 128 bytes
+    if constexpr (RB == 128) return row * 128 + ((ch ^ (row & 7)) << 4);
+    else return row * 64 + ((ch ^ ((row >> 1) & 3)) << 4);  // 64-byte rows: two rows per 128 bytes
 }
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -78,27 +88,8 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int FA, int FB, bool BF16OUT>
-__global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs g) {
-    constexpr bool A4 = FA == E2M1, B4 = FB == E2M1;
-    constexpr int BK = (A4 && B4) ? 256 : 128;  // K elements per tile
-    constexpr int RBA = A4 ? BK / 2 : BK;       // LDS row bytes
-    constexpr int RBB = B4 ? BK / 2 : BK;
-    constexpr int SB = BK / 32;                 // scale bytes per row per tile
-    constexpr int STEPS = BK / 64;              // MFMAs along K per tile
-    constexpr int CPRA = RBA / 16, CPRB = RBB / 16;
-    constexpr int NLA = BM * CPRA / NT, NLB = BN * CPRB / NT;
-
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * RBA];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * RBB];
-    __shared__ __attribute__((aligned(16))) uint8_t sAs[2][BM * SB];
-    __shared__ __attribute__((aligned(16))) uint8_t sBs[2][BN * SB];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int l32 = lane & 31, h = lane >> 5;
-
-    // XCD-aware tile order
+// XCD-aware tile order: wg -> (tile row, tile column)
+__device__ __forceinline__ void tile_of(const GemmArgs &g, int &m0, int &n0) {
     const int ntiles = g.tiles_m * g.tiles_n;
     const int wg = blockIdx.x;
     const int xcd = wg & 7, idx = wg >> 3;
@@ -110,20 +101,22 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs g) {
     const int first_m = grp * GROUP;
     const int gsz = (g.tiles_m - first_m) < GROUP ? (g.tiles_m - first_m) : GROUP;
     const int in_grp = lt - grp * group_tiles;
-    const int tm = first_m + in_grp % gsz;
-    const int tn = in_grp / gsz;
-    const int m0 = tm * BM, n0 = tn * BN;
+    m0 = (first_m + in_grp % gsz) * BM;
+    n0 = (in_grp / gsz) * BN;
+}
 
-    const int K = g.K;
-    const int64_t rowA = A4 ? K / 2 : K, rowB = B4 ? K / 2 : K;
-    const int kblocks = K / 32;
-    const int ntk = (K + BK - 1) / BK;
-    const bool scale_vec = (kblocks % SB == 0) && (((uintptr_t)g.as | (uintptr_t)g.bs) % SB == 0);
-
+// Global -> register -> LDS staging of one K tile of codes (RBA / RBB bytes
+// per row) and scales (SB bytes per row) for the A and B tiles.
+template <int RBA, int RBB, int SB>
+struct Stager {
+    static constexpr int CPRA = RBA / 16, CPRB = RBB / 16;
+    static constexpr int NLA = BM * CPRA / NT, NLB = BN * CPRB / NT;
     uint4 ra[NLA], rb[NLB];
     uint32_t rsa[SB / 4], rsb[SB / 4];
 
-    auto load_tile = [&](int kt) {
+    __device__ __forceinline__ void load(const GemmArgs &g, int m0, int n0, int kt, int64_t rowA, int64_t rowB,
+                                         int kblocks, bool scale_vec) {
+        const int tid = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < NLA; i++) {
             const int id = tid + NT * i, row = id / CPRA, ch = id % CPRA;
@@ -167,26 +160,60 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs g) {
                 rsb[q] = vb;
             }
         }
-    };
+    }
 
-    auto store_tile = [&](int buf) {
+    __device__ __forceinline__ void store(uint8_t *sA, uint8_t *sB, uint8_t *sAs, uint8_t *sBs) {
+        const int tid = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < NLA; i++) {
             const int id = tid + NT * i, row = id / CPRA, ch = id % CPRA;
-            *reinterpret_cast<uint4 *>(&sA[buf][swz<RBA>(row, ch)]) = ra[i];
+            *reinterpret_cast<uint4 *>(&sA[swz<RBA>(row, ch)]) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < NLB; i++) {
             const int id = tid + NT * i, row = id / CPRB, ch = id % CPRB;
-            *reinterpret_cast<uint4 *>(&sB[buf][swz<RBB>(row, ch)]) = rb[i];
+            *reinterpret_cast<uint4 *>(&sB[swz<RBB>(row, ch)]) = rb[i];
         }
 #pragma unroll
         for (int q = 0; q < SB / 4; q++) {
-            reinterpret_cast<uint32_t *>(&sAs[buf][tid * SB])[q] = rsa[q];
-            reinterpret_cast<uint32_t *>(&sBs[buf][tid * SB])[q] = rsb[q];
+            reinterpret_cast<uint32_t *>(&sAs[tid * SB])[q] = rsa[q];
+            reinterpret_cast<uint32_t *>(&sBs[tid * SB])[q] = rsb[q];
         }
-    };
+    }
+};
 
+template <bool BF16OUT>
+__device__ __forceinline__ void store_c(const GemmArgs &g, int m, int n, float v) {
+    if (m < g.M && n < g.N) {
+        if (BF16OUT)
+            reinterpret_cast<uint16_t *>(g.c)[(int64_t)m * g.ldc + n] = (uint16_t)bf16_rne(v);
+        else
+            reinterpret_cast<float *>(g.c)[(int64_t)m * g.ldc + n] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 x E2M1 on the block-scaled matrix instruction.
+template <bool BF16OUT>
+__global__ __launch_bounds__(NT, 1) void k_gemm_fp4(GemmArgs g) {
+    constexpr int BK = 256, RB = 128, SB = 8, STEPS = 4;  // 256 FP4 = 128 bytes per row per tile
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * RB];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * RB];
+    __shared__ __attribute__((aligned(16))) uint8_t sAs[2][BM * SB];
+    __shared__ __attribute__((aligned(16))) uint8_t sBs[2][BN * SB];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    int m0, n0;
+    tile_of(g, m0, n0);
+
+    const int64_t rowA = g.K / 2, rowB = g.K / 2;
+    const int kblocks = g.K / 32;
+    const int ntk = (g.K + BK - 1) / BK;
+    const bool scale_vec = (kblocks % SB == 0) && (((uintptr_t)g.as | (uintptr_t)g.bs) % SB == 0);
+
+    Stager<RB, RB, SB> st;
     v16f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -196,13 +223,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs g) {
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
     auto compute = [&](int buf) {
-        // per-lane scale words: byte 2s of (word >> 8h) is block 2s + h of this tile
-        uint32_t sa[4][SB / 4], sbw[4][SB / 4];
+        // per-lane scale words: byte 2s' of (word >> 8h) is block 2s' + h of the word
+        uint32_t sa[4][2], sbw[4][2];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int ra_ = wm * 128 + i * 32 + l32, rb_ = wn * 128 + i * 32 + l32;
 #pragma unroll
-            for (int q = 0; q < SB / 4; q++) {
+            for (int q = 0; q < 2; q++) {
                 sa[i][q] = reinterpret_cast<const uint32_t *>(&sAs[buf][ra_ * SB])[q] >> (8 * h);
                 sbw[i][q] = reinterpret_cast<const uint32_t *>(&sBs[buf][rb_ * SB])[q] >> (8 * h);
             }
@@ -212,66 +239,240 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs g) {
             v8i fa[4], fb[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int row = wm * 128 + i * 32 + l32;
-                if constexpr (A4) {
-                    const uint4 t = *reinterpret_cast<const uint4 *>(&sA[buf][swz<RBA>(row, 2 * s + h)]);
-                    fa[i] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
-                } else {
-                    const uint4 t0 = *reinterpret_cast<const uint4 *>(&sA[buf][swz<RBA>(row, 4 * s + h)]);
-                    const uint4 t1 = *reinterpret_cast<const uint4 *>(&sA[buf][swz<RBA>(row, 4 * s + 2 + h)]);
-                    fa[i] = v8i{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w, (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-                }
+                const uint4 t = *reinterpret_cast<const uint4 *>(&sA[buf][swz<RB>(wm * 128 + i * 32 + l32, 2 * s + h)]);
+                fa[i] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
             }
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const int row = wn * 128 + j * 32 + l32;
-                if constexpr (B4) {
-                    const uint4 t = *reinterpret_cast<const uint4 *>(&sB[buf][swz<RBB>(row, 2 * s + h)]);
-                    fb[j] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
-                } else {
-                    const uint4 t0 = *reinterpret_cast<const uint4 *>(&sB[buf][swz<RBB>(row, 4 * s + h)]);
-                    const uint4 t1 = *reinterpret_cast<const uint4 *>(&sB[buf][swz<RBB>(row, 4 * s + 2 + h)]);
-                    fb[j] = v8i{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w, (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-                }
+                const uint4 t = *reinterpret_cast<const uint4 *>(&sB[buf][swz<RB>(wn * 128 + j * 32 + l32, 2 * s + h)]);
+                fb[j] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
             }
-            constexpr int q = (2 * s) / 4;        // scale word holding blocks 2s, 2s+1
-            constexpr int sel = (2 * s) % 4;      // its byte, after the >> 8h above
+            constexpr int q = s / 2, sel = (2 * s) % 4;
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
                 for (int j = 0; j < 4; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fa[i], fb[j], acc[i][j], MfmaFmt<FA>::v, MfmaFmt<FB>::v, sel, (int)sa[i][q], sel,
-                        (int)sbw[j][q]);
+                        fa[i], fb[j], acc[i][j], 4, 4, sel, (int)sa[i][q], sel, (int)sbw[j][q]);
         });
     };
 
-    load_tile(0);
-    store_tile(0);
+    st.load(g, m0, n0, 0, rowA, rowB, kblocks, scale_vec);
+    st.store(sA[0], sB[0], sAs[0], sBs[0]);
     __syncthreads();
     for (int kt = 0; kt < ntk; kt++) {
         const int cur = kt & 1;
-        if (kt + 1 < ntk) load_tile(kt + 1);
+        if (kt + 1 < ntk) st.load(g, m0, n0, kt + 1, rowA, rowB, kblocks, scale_vec);
         compute(cur);
-        if (kt + 1 < ntk) store_tile(cur ^ 1);
+        if (kt + 1 < ntk) st.store(sA[cur ^ 1], sB[cur ^ 1], sAs[cur ^ 1], sBs[cur ^ 1]);
         __syncthreads();
     }
 
-    // epilogue: lane holds column n = l32 and rows 8(r/4) + 4h + r%4 of each 32 x 32 tile
+    // lane holds column n = l32 and rows 8(r/4) + 4h + r%4 of each 32 x 32 tile
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                store_c<BF16OUT>(g, m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3),
+                                 n0 + wn * 128 + j * 32 + l32, acc[i][j][r]);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 carrier: any pair with an FP8 operand.
+
+// 8 codes of one lane (bytes of `lo`, `hi` for FP8; nibbles of `lo` for E2M1)
+// -> 8 bf16 = code * scale (scale a normal power of two: exact)
+template <int F>
+__device__ __forceinline__ v8bf to_bf16x8(uint32_t lo, uint32_t hi, float scale) {
+    v2bf p0, p1, p2, p3;
+    if constexpr (F == E4M3) {
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+    } else if constexpr (F == E5M2) {
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(lo, scale, false);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(lo, scale, true);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(hi, scale, false);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(hi, scale, true);
+    } else {
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(lo, scale, 0);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(lo, scale, 1);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(lo, scale, 2);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(lo, scale, 3);
+    }
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// the 8 codes of row `row`, elements [16s + 8h, 16s + 8h + 8) of the K tile
+template <int F, int RB>
+__device__ __forceinline__ void read_codes(const uint8_t *tile, int row, int s, int h, uint32_t &lo, uint32_t &hi) {
+    if constexpr (F == E2M1) {
+        const int byte = 8 * s + 4 * h;  // 4 bytes
+        lo = *reinterpret_cast<const uint32_t *>(&tile[swz<RB>(row, byte >> 4) + (byte & 15)]);
+        hi = 0;
+    } else {
+        const int byte = 16 * s + 8 * h;  // 8 bytes
+        const uint2 t = *reinterpret_cast<const uint2 *>(&tile[swz<RB>(row, byte >> 4) + (byte & 15)]);
+        lo = t.x;
+        hi = t.y;
+    }
+}
+
+// WIDE = false: the fast path, for tiles whose scales fit the carrier;
+// WIDE = true: the exact per-block path, for the other tiles.  Both kernels
+// are launched; each returns at once on the tiles that belong to the other.
+template <int FA, int FB, bool BF16OUT, bool WIDE>
+__global__ __launch_bounds__(NT, 1) void k_gemm_carrier(GemmArgs g) {
+    constexpr int BK = 128, SB = 4, SUB = BK / 16;  // 16 K per bf16 instruction
+    constexpr int RBA = FA == E2M1 ? 64 : 128, RBB = FB == E2M1 ? 64 : 128;
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * RBA];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * RBB];
+    __shared__ __attribute__((aligned(16))) uint8_t sAs[2][BM * SB];
+    __shared__ __attribute__((aligned(16))) uint8_t sBs[2][BN * SB];
+    __shared__ int sRa[BM], sRb[BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    int m0, n0;
+    tile_of(g, m0, n0);
+
+    const int64_t rowA = FA == E2M1 ? g.K / 2 : g.K, rowB = FB == E2M1 ? g.K / 2 : g.K;
+    const int kblocks = g.K / 32;
+    const int ntk = (g.K + BK - 1) / BK;
+    const bool scale_vec = (kblocks % SB == 0) && (((uintptr_t)g.as | (uintptr_t)g.bs) % SB == 0);
+
+    // reference scales R = max over the row's blocks; the tile is "wide" if a
+    // row's scales spread over more than kSpreadMax binades or hold 0xFF
+    bool wide;
+    {
+        const int ga = min(m0 + tid, g.M - 1), gb = min(n0 + tid, g.N - 1);
+        int amax = 0, amin = 255, bmax = 0, bmin = 255;
+        const uint8_t *pa = g.as + (int64_t)ga * kblocks, *pb = g.bs + (int64_t)gb * kblocks;
+        for (int kb = 0; kb < kblocks; kb++) {
+            const int a = pa[kb], b = pb[kb];
+            amax = max(amax, a); amin = min(amin, a);
+            bmax = max(bmax, b); bmin = min(bmin, b);
+        }
+        sRa[tid] = amax;
+        sRb[tid] = bmax;
+        const bool w = amax - amin > kSpreadMax || bmax - bmin > kSpreadMax || amax == 255 || bmax == 255;
+        wide = __syncthreads_or(w) != 0;
+    }
+    if (wide != WIDE) return;  // uniform across the workgroup
+
+    Stager<RBA, RBB, SB> st;
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    // fast path: a' = code * 2^(S - R) for this lane's row, 4 blocks per tile
+    auto compute_fast = [&](int buf) {
+        float sca[4][4], scb[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int ra_ = wm * 128 + i * 32 + l32, rb_ = wn * 128 + i * 32 + l32;
+            const uint32_t wa = *reinterpret_cast<const uint32_t *>(&sAs[buf][ra_ * SB]);
+            const uint32_t wb = *reinterpret_cast<const uint32_t *>(&sBs[buf][rb_ * SB]);
+            const int Ra = sRa[ra_], Rb = sRb[rb_];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                sca[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wa >> (8 * q)) & 0xFF) - Ra);
+                scb[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wb >> (8 * q)) & 0xFF) - Rb);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < SUB; s++) {
+            v8bf fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                uint32_t lo, hi;
+                read_codes<FA, RBA>(sA[buf], wm * 128 + i * 32 + l32, s, h, lo, hi);
+                fa[i] = to_bf16x8<FA>(lo, hi, sca[i][s >> 1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                uint32_t lo, hi;
+                read_codes<FB, RBB>(sB[buf], wn * 128 + j * 32 + l32, s, h, lo, hi);
+                fb[j] = to_bf16x8<FB>(lo, hi, scb[j][s >> 1]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // exact path: per block, partial sum of unscaled codes, then ldexp by S_a + S_b
+    // (the block loop stays rolled to bound register pressure; only the tile
+    // loops that index the accumulators are unrolled)
+    auto compute_wide = [&](int buf) {
+#pragma unroll 1
+        for (int blk = 0; blk < BK / 32; blk++) {
+            static_for<0, 4>([&](auto ii) {
+                constexpr int i = decltype(ii)::value;
+                int sa_r[16];
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    sa_r[r] = sAs[buf][(wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * SB + blk];
+                static_for<0, 4>([&](auto jj) {
+                    constexpr int j = decltype(jj)::value;
+                    v16f p;
+#pragma unroll
+                    for (int r = 0; r < 16; r++) p[r] = 0.f;
+#pragma unroll
+                    for (int s = 0; s < 2; s++) {
+                        uint32_t lo, hi;
+                        read_codes<FA, RBA>(sA[buf], wm * 128 + i * 32 + l32, 2 * blk + s, h, lo, hi);
+                        const v8bf a8 = to_bf16x8<FA>(lo, hi, 1.0f);
+                        read_codes<FB, RBB>(sB[buf], wn * 128 + j * 32 + l32, 2 * blk + s, h, lo, hi);
+                        const v8bf b8 = to_bf16x8<FB>(lo, hi, 1.0f);
+                        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, p, 0, 0, 0);
+                    }
+                    const int sb = sBs[buf][(wn * 128 + j * 32 + l32) * SB + blk];
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const float v = __builtin_amdgcn_ldexpf(p[r], sa_r[r] + sb - 254);
+                        acc[i][j][r] += (sa_r[r] == 255 || sb == 255) ? __builtin_nanf("") : v;
+                    }
+                });
+            });
+        }
+    };
+
+    st.load(g, m0, n0, 0, rowA, rowB, kblocks, scale_vec);
+    st.store(sA[0], sB[0], sAs[0], sBs[0]);
+    __syncthreads();
+    for (int kt = 0; kt < ntk; kt++) {
+        const int cur = kt & 1;
+        if (kt + 1 < ntk) st.load(g, m0, n0, kt + 1, rowA, rowB, kblocks, scale_vec);
+        if constexpr (WIDE)
+            compute_wide(cur);
+        else
+            compute_fast(cur);
+        if (kt + 1 < ntk) st.store(sA[cur ^ 1], sB[cur ^ 1], sAs[cur ^ 1], sBs[cur ^ 1]);
+        __syncthreads();
+    }
+
 #pragma unroll
     for (int i = 0; i < 4; i++) {
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const int n = n0 + wn * 128 + j * 32 + l32;
+            const int nl = wn * 128 + j * 32 + l32;
+            const int Rb = sRb[nl];
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < g.M && n < g.N) {
-                    if (BF16OUT)
-                        reinterpret_cast<uint16_t *>(g.c)[(int64_t)m * g.ldc + n] = (uint16_t)bf16_rne(acc[i][j][r]);
-                    else
-                        reinterpret_cast<float *>(g.c)[(int64_t)m * g.ldc + n] = acc[i][j][r];
-                }
+                const int ml = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const float v = WIDE ? acc[i][j][r] : __builtin_amdgcn_ldexpf(acc[i][j][r], sRa[ml] + Rb - 254);
+                store_c<BF16OUT>(g, m0 + ml, n0 + nl, v);
             }
         }
     }
@@ -292,10 +493,20 @@ __global__ void k_zero(void *c, int64_t ldc, int M, int N) {
 template <int FA, int FB>
 hipError_t launch_fmt(const GemmArgs &g, bool bf16, hipStream_t stream) {
     const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(NT);
-    if (bf16)
-        hipLaunchKernelGGL((k_gemm<FA, FB, true>), grid, block, 0, stream, g);
-    else
-        hipLaunchKernelGGL((k_gemm<FA, FB, false>), grid, block, 0, stream, g);
+    if constexpr (FA == E2M1 && FB == E2M1) {
+        if (bf16)
+            hipLaunchKernelGGL((k_gemm_fp4<true>), grid, block, 0, stream, g);
+        else
+            hipLaunchKernelGGL((k_gemm_fp4<false>), grid, block, 0, stream, g);
+    } else {
+        if (bf16) {
+            hipLaunchKernelGGL((k_gemm_carrier<FA, FB, true, false>), grid, block, 0, stream, g);
+            hipLaunchKernelGGL((k_gemm_carrier<FA, FB, true, true>), grid, block, 0, stream, g);
+        } else {
+            hipLaunchKernelGGL((k_gemm_carrier<FA, FB, false, false>), grid, block, 0, stream, g);
+            hipLaunchKernelGGL((k_gemm_carrier<FA, FB, false, true>), grid, block, 0, stream, g);
+        }
+    }
     return hipGetLastError();
 }
 
@@ -310,9 +521,8 @@ hipError_t launch_fa(const GemmArgs &g, int fb, bool bf16, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t *a, const uint8_t *as, int fa, const uint8_t *b, const uint8_t *bs,
-                       int fb, int64_t M, int64_t N, int64_t K, void *c, bool bf16_out, int64_t ldc,
-                       hipStream_t stream) {
+hipError_t launch_gemm(const uint8_t *a, const uint8_t *as, int fa, const uint8_t *b, const uint8_t *bs, int fb,
+                       int64_t M, int64_t N, int64_t K, void *c, bool bf16_out, int64_t ldc, hipStream_t stream) {
     if (K == 0) {
         const int64_t n = M * N;
         const dim3 grid((unsigned)((n + 255) / 256));

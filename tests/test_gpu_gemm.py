@@ -162,3 +162,47 @@ def test_full_size_sampled_rows(mx, ci, gname, bf16):
     C, S = oracle.gemm(qa[0], qa[1], qa_spec.fmt, qb[0], qb[1], qb_spec.fmt, rows=rows)
     r = check_gemm(c[rows], C, S, bf16)
     print("max |err|/S", r, flush=True)
+
+
+def _random_codes(rng, rows, K, fmt):
+    if fmt == "e2m1":
+        c = rng.integers(0, 256, (rows, K // 2)).astype(np.uint8)
+    else:
+        c = rng.integers(0, 256, (rows, K)).astype(np.uint8)
+        bad = (c & 0x7F) == 0x7F if fmt == "e4m3" else (c & 0x7C) == 0x7C
+        c[bad] = 0x38
+    return c
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e2m1"), ("e2m1", "e5m2")])
+@pytest.mark.parametrize("spread", ["narrow", "full", "pathological"])
+def test_scale_spreads(mx, fa, fb, spread):
+    """codes and E8M0 scales drawn directly: narrow spreads (carrier fast path),
+    spreads of up to 90 binades per row (exact per-block path), and rows whose
+    only contributions come from blocks 2^100 below the row's largest scale"""
+    rng = np.random.default_rng(["narrow", "full", "pathological"].index(spread) * 10 + FMTS.index(fa))
+    M, N, K = 288, 320, 512
+    ca, cb = _random_codes(rng, M, K, fa), _random_codes(rng, N, K, fb)
+    if spread == "narrow":
+        sa = rng.integers(110, 140, (M, K // 32)).astype(np.uint8)
+        sb = rng.integers(110, 140, (N, K // 32)).astype(np.uint8)
+    elif spread == "full":
+        # per-row spreads up to 90 binades (exact per-block path) while every
+        # result stays inside the fp32 normal range the output can hold
+        sa = rng.integers(80, 171, (M, K // 32)).astype(np.uint8)
+        sb = rng.integers(80, 171, (N, K // 32)).astype(np.uint8)
+    else:
+        sa = rng.integers(120, 135, (M, K // 32)).astype(np.uint8)
+        sb = rng.integers(120, 135, (N, K // 32)).astype(np.uint8)
+        sa[:, 0] = 230                      # one huge block per A row ...
+        cbz = cb.copy()
+        nb = 16 if fb == "e2m1" else 32
+        cbz[:, :nb] = 0                     # ... where every B column is zero
+        cb = cbz
+        sa[:, 1:] = rng.integers(10, 30, (M, K // 32 - 1))   # the rest ~2^-100 smaller
+    C, S = oracle.gemm(ca, sa, fa, cb, sb, fb)
+    assert np.all(np.isfinite(C))
+    for bf16 in (False, True):
+        c = _host_c(_run(mx, (ca, sa), fa, (cb, sb), fb, bf16), bf16)
+        r = check_gemm(c, C, S, bf16)
+        print(spread, fa, fb, "bf16" if bf16 else "f32", "max |err|/S", r)
