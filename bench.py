@@ -40,6 +40,14 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
 CONFIGS = (1, 2, 3)  # the three Llama-3.1-8B workloads
 WORKLOAD = "llama31_8b_linear_set"
+PROFILE_COMMANDS = (
+    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace -- "
+    "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch -- "
+    "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write -- "
+    "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
+)
 
 
 def quant_bytes(rows: int, cols: int, fmt: str) -> float:
@@ -170,6 +178,86 @@ def cpu_baseline(seed: int, step_flops: float) -> dict:
             "sample": "; ".join(parts) + "; per-step time extrapolated to %.1f s" % t_total}
 
 
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError("%s/*%s" % (d, suffix))
+
+
+def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, command: str) -> None:
+    """Turn rocprofv3 CSV output (kernel trace with stats; FETCH_SIZE and
+    WRITE_SIZE counter passes with --calibrate-copy) into the short summaries
+    kept under profiles/: per-kernel average durations, and HBM bytes per
+    launch scaled by what the counters read for the 256 MiB copy."""
+    stats = _read_csv(_find(trace_dir, "kernel_stats.csv"))
+    fetch = _read_csv(_find(fetch_dir, "counter_collection.csv"))
+    write = _read_csv(_find(write_dir, "counter_collection.csv"))
+
+    def per_kernel(rows):
+        out = {}
+        for r in rows:
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    f_kib, w_kib = per_kernel(fetch), per_kernel(write)
+    copy = [k for k in f_kib if "copyBuffer" in k or "copy" in k.lower()]
+    if not copy:
+        raise RuntimeError("no copy kernel in the counter passes (run bench.py with --calibrate-copy)")
+    known_kib = 256 * 1024.0
+    f_scale, w_scale = known_kib / f_kib[copy[0]], known_kib / w_kib[copy[0]]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    lines = ["# rocprofv3 kernel trace: %s" % WORKLOAD, "",
+             "Command (from the repository root on the GPU box):", "", "    " + command[0], "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
+            r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_%s.md" % WORKLOAD), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    kern = {}
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE): %s" % WORKLOAD, "",
+             "Commands (from the repository root on the GPU box), one counter per run:", "",
+             "    " + command[1], "    " + command[2], "",
+             "Calibration: a plain 256 MiB device copy (`%s`) reads FETCH_SIZE = %.0f KiB and "
+             "WRITE_SIZE = %.0f KiB per dispatch for 262144 KiB read and written, so counter KiB are "
+             "scaled by %.4f (fetch) and %.4f (write)." % (copy[0], f_kib[copy[0]], w_kib[copy[0]], f_scale, w_scale),
+             "", "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (MB) | written (MB) |", "|---|---|---|---|---|"]
+    for k in f_kib:
+        if k in copy or "mx::" not in k:
+            continue
+        rd, wr = f_kib[k] * f_scale * 1024, w_kib.get(k, 0.0) * w_scale * 1024
+        kern[k] = {"read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr}
+        lines.append("| `%s` | %.0f | %.0f | %.1f | %.1f |" % (k, f_kib[k], w_kib.get(k, 0.0), rd / 1e6, wr / 1e6))
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % WORKLOAD), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump({"source_sha": kernel_source_sha(), "workload": WORKLOAD, "fetch_scale": f_scale,
+                   "write_scale": w_scale, "kernels": kern, "commands": command[1:]}, f, indent=1)
+
+
+# the kernel symbol each bench launch name runs (dominant kernel lookup in traffic.json)
+def kernel_symbol(name: str) -> str:
+    fa, fb = None, None
+    if "mx_gemm" in name:
+        fa, fb = name.split()[-1].split("x")
+        code = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
+        out = "true" if "/Y " in name else "false"
+        mode = 0 if fa == fb == "e2m1" else 1
+        return "void mx::(anonymous namespace)::pipe::k_gemm_pipe<%d, %d, %s, %d>(mx::GemmArgs)" % (
+            code[fa], code[fb], out, mode)
+    return name
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,7 +266,14 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=workloads.DEFAULT_SEED)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table to stderr")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV output and exit")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a plain 256 MiB device copy three times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, command=PROFILE_COMMANDS)
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: the hot path runs on a single MI355X and this build "
               "has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -212,6 +307,13 @@ def main() -> int:
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     print("bench: timed %d steps, %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
 
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
     kernels = []
     for i, (name, kind, work, _) in enumerate(step.launches):
         ms = float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
@@ -229,7 +331,7 @@ def main() -> int:
             kernels.append(k)
 
     dom = max(kernels, key=lambda k: k["ms"])
-    traffic = measured_traffic(dom["kernel"])
+    traffic = measured_traffic(kernel_symbol(dom["kernel"]))
     roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3), "peak": dom["peak"],
                 "unit": dom["unit"], "frac": round(dom["frac"], 4), "traffic": traffic, "kernel": dom["kernel"]}
     q = [k for k in kernels if k["bound"] == "hbm"]

@@ -1,0 +1,856 @@
+// mx_gemm_kernels.h -- MX-scaled GEMM kernels for gfx950: C[m, n] = sum_k A[m, k] * B[n, k],
+// both operands MX-quantized with K contiguous (codes + one E8M0 scale per
+// 32-element block), fp32 accumulation, fp32 or bf16 output.
+//
+// The linear-layer GEMMs (forward, activation gradient, weight gradient) of
+// quantized training (FP4-training article on hzrcw.cc, section 02), which
+// the Primus page identifies as the dominant training cost.
+//
+// Two kernels share one tiling (MFMA-bound; 2*M*N*K flops):
+//   - workgroup tile 256 x 256, four waves of 128 x 128 (4 x 4 tiles of
+//     32 x 32, 256 fp32 accumulators per lane);
+//   - operand codes and scales double-buffered in LDS, the 16-byte chunks of
+//     each code row XOR-swizzled by the row index so that the lanes reading
+//     one K chunk of consecutive rows hit distinct banks; one barrier per K
+//     tile, the next tile's global loads in flight during the current tile's
+//     matrix work;
+//   - workgroups are dealt round-robin to the 8 XCDs, so each XCD gets a
+//     contiguous run of tiles, ordered in groups of 8 tile rows, to keep shared
+//     A rows and B columns in that XCD's L2;
+//   - M and N tails: loads clamp to the last valid row, stores are masked; the
+//     K tail is zero-filled (code 0, scale byte 0).
+//
+// k_gemm_fp4 (E2M1 x E2M1): V_MFMA_SCALE_F32_32X32X64_F8F6F4.  Lane l serves
+// row l % 32 of A (column of B); its half h = l / 32 holds K[32h, 32h+32) of
+// the 64-element step -- one whole MX block -- and supplies that block's
+// E8M0 byte; the matrix core applies both scales.  Measured on gfx950: the
+// products of two E2M1 values span few enough binades that the instruction's
+// internal sum is exact, so only the fp32 accumulation rounds.
+//
+// k_gemm_carrier (any pair with an FP8 operand): measured on gfx950, the
+// scaled instruction sums the products of an FP8 block in a fixed-point
+// window about 13 bits below the largest product (1 + 2^-13 survives, 1 +
+// 2^-14 does not), an error of up to ~1e-4 of sum |a*b| on random codes --
+// outside the fp32 accumulation tolerance this library is held to.  So FP8
+// codes travel as bf16 (every E4M3 / E5M2 / E2M1 value times a power of two
+// in [2^-40, 1] is an exact bf16) through V_MFMA_F32_32X32X16_BF16, whose
+// 16-product sum is exact with one fp32 rounding:
+//   a'[m, k] = code * 2^(S_a[m, b] - R_a[m]),  R_a[m] = max_b S_a[m, b]
+// (V_CVT_SCALEF32_PK_BF16_{FP8,BF8,FP4}: two codes per instruction, exact for
+// normal power-of-two scales), same for B, and C = 2^(R_a + R_b - 254) *
+// sum a' b'.  A tile in which some row's scales spread over more than 40
+// binades, or which holds an E8M0 NaN (0xFF), is left to a second kernel with
+// an exact per-block path: each 32-element block's partial sum of unscaled
+// codes is scaled with ldexp and added in fp32 (separate kernels keep the
+// VALU-side accumulation out of the fast kernel's register budget).
+#pragma once
+#include <type_traits>
+
+#include "mx_internal.h"
+
+namespace mx {
+
+struct GemmArgs {
+    const uint8_t *a, *as, *b, *bs;
+    void *c;
+    int64_t ldc;
+    int M, N, K;
+    int tiles_m, tiles_n;
+};
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int BM = 256, BN = 256, NT = 256;
+constexpr int kSpreadMax = 40;  // carrier fast path: per-row scale spread, binades
+
+// compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N)
+template <int I, int N, class Fn>
+__device__ __forceinline__ void static_for(Fn &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// byte offset of 16-byte chunk `ch` of row `row` in a swizzled LDS tile
+template <int RB>
+__device__ __forceinline__ int swz_key(int row) {
+    if constexpr (RB == 128) return row & 7;
+    else if constexpr (RB == 64) return (row >> 1) & 3;  // two rows per 128 bytes
+    else return (row >> 2) & 1;                          // 32-byte rows: four rows per 128 bytes
+}
+template <int RB>
+__device__ __forceinline__ int swz(int row, int ch) {
+    return row * RB + ((ch ^ swz_key<RB>(row)) << 4);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// XCD-aware tile order: wg -> (tile row, tile column)
+__device__ __forceinline__ void tile_of(const GemmArgs &g, int &m0, int &n0) {
+    const int ntiles = g.tiles_m * g.tiles_n;
+    const int wg = blockIdx.x;
+    const int xcd = wg & 7, idx = wg >> 3;
+    const int per = ntiles >> 3, rem = ntiles & 7;
+    const int lt = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    constexpr int GROUP = 8;
+    const int group_tiles = GROUP * g.tiles_n;
+    const int grp = lt / group_tiles;
+    const int first_m = grp * GROUP;
+    const int gsz = (g.tiles_m - first_m) < GROUP ? (g.tiles_m - first_m) : GROUP;
+    const int in_grp = lt - grp * group_tiles;
+    m0 = (first_m + in_grp % gsz) * BM;
+    n0 = (in_grp / gsz) * BN;
+}
+
+// Global -> register -> LDS staging of one K tile of codes (RBA / RBB bytes
+// per row) and scales (SB bytes per row) for the A and B tiles.
+template <int RBA, int RBB, int SB>
+struct Stager {
+    static constexpr int CPRA = RBA / 16, CPRB = RBB / 16;
+    static constexpr int NLA = BM * CPRA / NT, NLB = BN * CPRB / NT;
+    uint4 ra[NLA], rb[NLB];
+    uint32_t rsa[SB / 4], rsb[SB / 4];
+
+    __device__ __forceinline__ void load(const GemmArgs &g, int m0, int n0, int kt, int64_t rowA, int64_t rowB,
+                                         int kblocks, bool scale_vec) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < NLA; i++) {
+            const int id = tid + NT * i, row = id / CPRA, ch = id % CPRA;
+            const int gr = min(m0 + row, g.M - 1);
+            const int64_t off = (int64_t)kt * RBA + ch * 16;
+            ra[i] = off < rowA ? *reinterpret_cast<const uint4 *>(g.a + gr * rowA + off) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NLB; i++) {
+            const int id = tid + NT * i, row = id / CPRB, ch = id % CPRB;
+            const int gr = min(n0 + row, g.N - 1);
+            const int64_t off = (int64_t)kt * RBB + ch * 16;
+            rb[i] = off < rowB ? *reinterpret_cast<const uint4 *>(g.b + gr * rowB + off) : make_uint4(0, 0, 0, 0);
+        }
+        // scales: thread t owns row t of the A and B tiles
+        const int ga = min(m0 + tid, g.M - 1), gb = min(n0 + tid, g.N - 1);
+        const int kb0 = kt * SB;
+        if (scale_vec && kb0 + SB <= kblocks) {
+            if constexpr (SB == 4) {
+                rsa[0] = *reinterpret_cast<const uint32_t *>(g.as + (int64_t)ga * kblocks + kb0);
+                rsb[0] = *reinterpret_cast<const uint32_t *>(g.bs + (int64_t)gb * kblocks + kb0);
+            } else {
+                const uint2 ta = *reinterpret_cast<const uint2 *>(g.as + (int64_t)ga * kblocks + kb0);
+                const uint2 tb = *reinterpret_cast<const uint2 *>(g.bs + (int64_t)gb * kblocks + kb0);
+                rsa[0] = ta.x; rsa[1] = ta.y;
+                rsb[0] = tb.x; rsb[1] = tb.y;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < SB / 4; q++) {
+                uint32_t va = 0, vb = 0;
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const int kb = kb0 + 4 * q + t;
+                    if (kb < kblocks) {
+                        va |= (uint32_t)g.as[(int64_t)ga * kblocks + kb] << (8 * t);
+                        vb |= (uint32_t)g.bs[(int64_t)gb * kblocks + kb] << (8 * t);
+                    }
+                }
+                rsa[q] = va;
+                rsb[q] = vb;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(uint8_t *sA, uint8_t *sB, uint8_t *sAs, uint8_t *sBs) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < NLA; i++) {
+            const int id = tid + NT * i, row = id / CPRA, ch = id % CPRA;
+            *reinterpret_cast<uint4 *>(&sA[swz<RBA>(row, ch)]) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NLB; i++) {
+            const int id = tid + NT * i, row = id / CPRB, ch = id % CPRB;
+            *reinterpret_cast<uint4 *>(&sB[swz<RBB>(row, ch)]) = rb[i];
+        }
+#pragma unroll
+        for (int q = 0; q < SB / 4; q++) {
+            reinterpret_cast<uint32_t *>(&sAs[tid * SB])[q] = rsa[q];
+            reinterpret_cast<uint32_t *>(&sBs[tid * SB])[q] = rsb[q];
+        }
+    }
+};
+
+template <bool BF16OUT>
+__device__ __forceinline__ void store_c(const GemmArgs &g, int m, int n, float v) {
+    if (m < g.M && n < g.N) {
+        if (BF16OUT)
+            reinterpret_cast<uint16_t *>(g.c)[(int64_t)m * g.ldc + n] = (uint16_t)bf16_rne(v);
+        else
+            reinterpret_cast<float *>(g.c)[(int64_t)m * g.ldc + n] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 x E2M1 on the block-scaled matrix instruction.
+template <bool BF16OUT>
+__global__ __launch_bounds__(NT, 1) void k_gemm_fp4(GemmArgs g) {
+    constexpr int BK = 256, RB = 128, SB = 8, STEPS = 4;  // 256 FP4 = 128 bytes per row per tile
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * RB];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * RB];
+    __shared__ __attribute__((aligned(16))) uint8_t sAs[2][BM * SB];
+    __shared__ __attribute__((aligned(16))) uint8_t sBs[2][BN * SB];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    int m0, n0;
+    tile_of(g, m0, n0);
+
+    const int64_t rowA = g.K / 2, rowB = g.K / 2;
+    const int kblocks = g.K / 32;
+    const int ntk = (g.K + BK - 1) / BK;
+    const bool scale_vec = (kblocks % SB == 0) && (((uintptr_t)g.as | (uintptr_t)g.bs) % SB == 0);
+
+    Stager<RB, RB, SB> st;
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    auto compute = [&](int buf) {
+        // per-lane scale words: byte 2s' of (word >> 8h) is block 2s' + h of the word
+        uint32_t sa[4][2], sbw[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int ra_ = wm * 128 + i * 32 + l32, rb_ = wn * 128 + i * 32 + l32;
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                sa[i][q] = reinterpret_cast<const uint32_t *>(&sAs[buf][ra_ * SB])[q] >> (8 * h);
+                sbw[i][q] = reinterpret_cast<const uint32_t *>(&sBs[buf][rb_ * SB])[q] >> (8 * h);
+            }
+        }
+        static_for<0, STEPS>([&](auto step) {
+            constexpr int s = decltype(step)::value;
+            v8i fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint4 t = *reinterpret_cast<const uint4 *>(&sA[buf][swz<RB>(wm * 128 + i * 32 + l32, 2 * s + h)]);
+                fa[i] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint4 t = *reinterpret_cast<const uint4 *>(&sB[buf][swz<RB>(wn * 128 + j * 32 + l32, 2 * s + h)]);
+                fb[j] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
+            }
+            constexpr int q = s / 2, sel = (2 * s) % 4;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fa[i], fb[j], acc[i][j], 4, 4, sel, (int)sa[i][q], sel, (int)sbw[j][q]);
+        });
+    };
+
+    st.load(g, m0, n0, 0, rowA, rowB, kblocks, scale_vec);
+    st.store(sA[0], sB[0], sAs[0], sBs[0]);
+    __syncthreads();
+    for (int kt = 0; kt < ntk; kt++) {
+        const int cur = kt & 1;
+        if (kt + 1 < ntk) st.load(g, m0, n0, kt + 1, rowA, rowB, kblocks, scale_vec);
+        compute(cur);
+        if (kt + 1 < ntk) st.store(sA[cur ^ 1], sB[cur ^ 1], sAs[cur ^ 1], sBs[cur ^ 1]);
+        __syncthreads();
+    }
+
+    // lane holds column n = l32 and rows 8(r/4) + 4h + r%4 of each 32 x 32 tile
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                store_c<BF16OUT>(g, m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3),
+                                 n0 + wn * 128 + j * 32 + l32, acc[i][j][r]);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 carrier: any pair with an FP8 operand.
+
+// 8 codes of one lane (bytes of `lo`, `hi` for FP8; nibbles of `lo` for E2M1)
+// -> 8 bf16 = code * scale (scale a normal power of two: exact)
+template <int F>
+__device__ __forceinline__ v8bf to_bf16x8(uint32_t lo, uint32_t hi, float scale) {
+    v2bf p0, p1, p2, p3;
+    if constexpr (F == E4M3) {
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+    } else if constexpr (F == E5M2) {
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(lo, scale, false);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(lo, scale, true);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(hi, scale, false);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(hi, scale, true);
+    } else {
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(lo, scale, 0);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(lo, scale, 1);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(lo, scale, 2);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(lo, scale, 3);
+    }
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// the 8 codes of row `row`, elements [16s + 8h, 16s + 8h + 8) of the K tile
+template <int F, int RB>
+__device__ __forceinline__ void read_codes(const uint8_t *tile, int row, int s, int h, uint32_t &lo, uint32_t &hi) {
+    if constexpr (F == E2M1) {
+        const int byte = 8 * s + 4 * h;  // 4 bytes
+        lo = *reinterpret_cast<const uint32_t *>(&tile[swz<RB>(row, byte >> 4) + (byte & 15)]);
+        hi = 0;
+    } else {
+        const int byte = 16 * s + 8 * h;  // 8 bytes
+        const uint2 t = *reinterpret_cast<const uint2 *>(&tile[swz<RB>(row, byte >> 4) + (byte & 15)]);
+        lo = t.x;
+        hi = t.y;
+    }
+}
+
+// WIDE = false: the fast path, for tiles whose scales fit the carrier;
+// WIDE = true: the exact per-block path, for the other tiles.  Both kernels
+// are launched; each returns at once on the tiles that belong to the other.
+template <int FA, int FB, bool BF16OUT, bool WIDE>
+__global__ __launch_bounds__(NT, 1) void k_gemm_carrier(GemmArgs g) {
+    constexpr int BK = 128, SB = 4, SUB = BK / 16;  // 16 K per bf16 instruction
+    constexpr int RBA = FA == E2M1 ? 64 : 128, RBB = FB == E2M1 ? 64 : 128;
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * RBA];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * RBB];
+    __shared__ __attribute__((aligned(16))) uint8_t sAs[2][BM * SB];
+    __shared__ __attribute__((aligned(16))) uint8_t sBs[2][BN * SB];
+    __shared__ int sRa[BM], sRb[BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    int m0, n0;
+    tile_of(g, m0, n0);
+
+    const int64_t rowA = FA == E2M1 ? g.K / 2 : g.K, rowB = FB == E2M1 ? g.K / 2 : g.K;
+    const int kblocks = g.K / 32;
+    const int ntk = (g.K + BK - 1) / BK;
+    const bool scale_vec = (kblocks % SB == 0) && (((uintptr_t)g.as | (uintptr_t)g.bs) % SB == 0);
+
+    // reference scales R = max over the row's blocks; the tile is "wide" if a
+    // row's scales spread over more than kSpreadMax binades or hold 0xFF
+    bool wide;
+    {
+        const int ga = min(m0 + tid, g.M - 1), gb = min(n0 + tid, g.N - 1);
+        int amax = 0, amin = 255, bmax = 0, bmin = 255;
+        const uint8_t *pa = g.as + (int64_t)ga * kblocks, *pb = g.bs + (int64_t)gb * kblocks;
+        for (int kb = 0; kb < kblocks; kb++) {
+            const int a = pa[kb], b = pb[kb];
+            amax = max(amax, a); amin = min(amin, a);
+            bmax = max(bmax, b); bmin = min(bmin, b);
+        }
+        sRa[tid] = amax;
+        sRb[tid] = bmax;
+        const bool w = amax - amin > kSpreadMax || bmax - bmin > kSpreadMax || amax == 255 || bmax == 255;
+        wide = __syncthreads_or(w) != 0;
+    }
+    if (wide != WIDE) return;  // uniform across the workgroup
+
+    Stager<RBA, RBB, SB> st;
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    // fast path: a' = code * 2^(S - R) for this lane's row, 4 blocks per tile
+    auto compute_fast = [&](int buf) {
+        float sca[4][4], scb[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int ra_ = wm * 128 + i * 32 + l32, rb_ = wn * 128 + i * 32 + l32;
+            const uint32_t wa = *reinterpret_cast<const uint32_t *>(&sAs[buf][ra_ * SB]);
+            const uint32_t wb = *reinterpret_cast<const uint32_t *>(&sBs[buf][rb_ * SB]);
+            const int Ra = sRa[ra_], Rb = sRb[rb_];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                sca[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wa >> (8 * q)) & 0xFF) - Ra);
+                scb[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wb >> (8 * q)) & 0xFF) - Rb);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < SUB; s++) {
+            v8bf fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                uint32_t lo, hi;
+                read_codes<FA, RBA>(sA[buf], wm * 128 + i * 32 + l32, s, h, lo, hi);
+                fa[i] = to_bf16x8<FA>(lo, hi, sca[i][s >> 1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                uint32_t lo, hi;
+                read_codes<FB, RBB>(sB[buf], wn * 128 + j * 32 + l32, s, h, lo, hi);
+                fb[j] = to_bf16x8<FB>(lo, hi, scb[j][s >> 1]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // exact path: per block, partial sum of unscaled codes, then ldexp by S_a + S_b
+    // (the block loop stays rolled to bound register pressure; only the tile
+    // loops that index the accumulators are unrolled)
+    auto compute_wide = [&](int buf) {
+#pragma unroll 1
+        for (int blk = 0; blk < BK / 32; blk++) {
+            static_for<0, 4>([&](auto ii) {
+                constexpr int i = decltype(ii)::value;
+                int sa_r[16];
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    sa_r[r] = sAs[buf][(wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * SB + blk];
+                static_for<0, 4>([&](auto jj) {
+                    constexpr int j = decltype(jj)::value;
+                    v16f p;
+#pragma unroll
+                    for (int r = 0; r < 16; r++) p[r] = 0.f;
+#pragma unroll
+                    for (int s = 0; s < 2; s++) {
+                        uint32_t lo, hi;
+                        read_codes<FA, RBA>(sA[buf], wm * 128 + i * 32 + l32, 2 * blk + s, h, lo, hi);
+                        const v8bf a8 = to_bf16x8<FA>(lo, hi, 1.0f);
+                        read_codes<FB, RBB>(sB[buf], wn * 128 + j * 32 + l32, 2 * blk + s, h, lo, hi);
+                        const v8bf b8 = to_bf16x8<FB>(lo, hi, 1.0f);
+                        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, p, 0, 0, 0);
+                    }
+                    const int sb = sBs[buf][(wn * 128 + j * 32 + l32) * SB + blk];
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const float v = __builtin_amdgcn_ldexpf(p[r], sa_r[r] + sb - 254);
+                        acc[i][j][r] += (sa_r[r] == 255 || sb == 255) ? __builtin_nanf("") : v;
+                    }
+                });
+            });
+        }
+    };
+
+    st.load(g, m0, n0, 0, rowA, rowB, kblocks, scale_vec);
+    st.store(sA[0], sB[0], sAs[0], sBs[0]);
+    __syncthreads();
+    for (int kt = 0; kt < ntk; kt++) {
+        const int cur = kt & 1;
+        if (kt + 1 < ntk) st.load(g, m0, n0, kt + 1, rowA, rowB, kblocks, scale_vec);
+        if constexpr (WIDE)
+            compute_wide(cur);
+        else
+            compute_fast(cur);
+        if (kt + 1 < ntk) st.store(sA[cur ^ 1], sB[cur ^ 1], sAs[cur ^ 1], sBs[cur ^ 1]);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int nl = wn * 128 + j * 32 + l32;
+            const int Rb = sRb[nl];
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int ml = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const float v = WIDE ? acc[i][j][r] : __builtin_amdgcn_ldexpf(acc[i][j][r], sRa[ml] + Rb - 254);
+                store_c<BF16OUT>(g, m0 + ml, n0 + nl, v);
+            }
+        }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Pipelined kernels (K a multiple of the stage depth, aligned pointers): the
+// same tiling and arithmetic as above, with operand tiles moved by
+// BUFFER_LOAD ... LDS (global memory straight to LDS, no register staging)
+// through NS = 4 LDS stages, so three K stages are in flight while one is
+// multiplied.  Stage depth: 64 code bytes per row (128 E2M1 or 64 FP8
+// elements; 32 bytes for an E2M1 operand paired with FP8).  Each stage has
+// its own LDS arrays, the loop is unrolled by NS so stage indices are
+// compile-time, and every stage load is issued unconditionally (past the last
+// tile the offset points outside the buffer and the load returns zeros), which
+// keeps the compiler's wait-count tracking exact: a wave waits only for the
+// stage it is about to read.  Rows past M or N also read as zeros through the
+// buffer's range check.
+namespace pipe {
+
+typedef __attribute__((address_space(3))) void *lds_t;
+constexpr int NS = 4;
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int SZ>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, void *lds, int voff, int soff) {
+    if constexpr (SZ == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)lds, 16, voff, soff, 0, 0);
+    else if constexpr (SZ == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)lds, 4, voff, soff, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)lds, 2, voff, soff, 0, 0);
+}
+
+// max and min of a row's E8M0 bytes (uint4 loads when aligned)
+__device__ __forceinline__ void row_scale_range(const uint8_t *p, int n, bool vec, int &mx, int &mn) {
+    mx = 0;
+    mn = 255;
+    if (vec) {
+        for (int k = 0; k < n; k += 16) {
+            const uint4 t = *reinterpret_cast<const uint4 *>(p + k);
+            const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+                const int b = (w[q >> 2] >> (8 * (q & 3))) & 0xFF;
+                mx = max(mx, b);
+                mn = min(mn, b);
+            }
+        }
+    } else {
+        for (int k = 0; k < n; k++) {
+            mx = max(mx, (int)p[k]);
+            mn = min(mn, (int)p[k]);
+        }
+    }
+}
+
+// MODE 0: E2M1 x E2M1, block-scaled instruction.  MODE 1: carrier fast path.
+// MODE 2: carrier exact per-block path (tiles the fast path leaves).
+template <int FA, int FB, bool BF16OUT, int MODE>
+__global__ __launch_bounds__(NT, 1) void k_gemm_pipe(GemmArgs g) {
+    constexpr bool A4 = FA == E2M1, B4 = FB == E2M1;
+    constexpr int KE = (A4 && B4) ? 128 : 64;          // K elements per stage
+    constexpr int RBA = A4 ? KE / 2 : KE, RBB = B4 ? KE / 2 : KE;
+    constexpr int SBY = KE / 32;                       // scale bytes per row per stage
+    constexpr int NIA = BM * RBA / 1024 / 4, NIB = BN * RBB / 1024 / 4;  // 1 KiB DMA per wave instruction
+    constexpr int LPS = NIA + NIB + 2;                 // DMA instructions per wave per stage
+    constexpr int CPRA = RBA / 16, CPRB = RBB / 16;
+
+    __shared__ __attribute__((aligned(16))) uint8_t sA0[BM * RBA], sA1[BM * RBA], sA2[BM * RBA], sA3[BM * RBA];
+    __shared__ __attribute__((aligned(16))) uint8_t sB0[BN * RBB], sB1[BN * RBB], sB2[BN * RBB], sB3[BN * RBB];
+    __shared__ __attribute__((aligned(16))) uint8_t sSA0[BM * 4], sSA1[BM * 4], sSA2[BM * 4], sSA3[BM * 4];
+    __shared__ __attribute__((aligned(16))) uint8_t sSB0[BN * 4], sSB1[BN * 4], sSB2[BN * 4], sSB3[BN * 4];
+    __shared__ int sRa[BM], sRb[BN];
+    auto stA = [&](auto S) -> uint8_t * {
+        constexpr int s = decltype(S)::value;
+        if constexpr (s == 0) return sA0; else if constexpr (s == 1) return sA1;
+        else if constexpr (s == 2) return sA2; else return sA3;
+    };
+    auto stB = [&](auto S) -> uint8_t * {
+        constexpr int s = decltype(S)::value;
+        if constexpr (s == 0) return sB0; else if constexpr (s == 1) return sB1;
+        else if constexpr (s == 2) return sB2; else return sB3;
+    };
+    auto stSA = [&](auto S) -> uint8_t * {
+        constexpr int s = decltype(S)::value;
+        if constexpr (s == 0) return sSA0; else if constexpr (s == 1) return sSA1;
+        else if constexpr (s == 2) return sSA2; else return sSA3;
+    };
+    auto stSB = [&](auto S) -> uint8_t * {
+        constexpr int s = decltype(S)::value;
+        if constexpr (s == 0) return sSB0; else if constexpr (s == 1) return sSB1;
+        else if constexpr (s == 2) return sSB2; else return sSB3;
+    };
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    int m0, n0;
+    tile_of(g, m0, n0);
+
+    const int rowA = A4 ? g.K / 2 : g.K, rowB = B4 ? g.K / 2 : g.K;
+    const int kblocks = g.K / 32;
+    const int ntk = g.K / KE;
+    const int mrows = min(BM, g.M - m0), nrows = min(BN, g.N - n0);
+    const uint32_t nrecA = (uint32_t)mrows * rowA, nrecB = (uint32_t)nrows * rowB;
+    const uint32_t nrecSA = (uint32_t)mrows * kblocks, nrecSB = (uint32_t)nrows * kblocks;
+    const __amdgpu_buffer_rsrc_t rA = rsrc(g.a + (int64_t)m0 * rowA, nrecA);
+    const __amdgpu_buffer_rsrc_t rB = rsrc(g.b + (int64_t)n0 * rowB, nrecB);
+    const __amdgpu_buffer_rsrc_t rSA = rsrc(g.as + (int64_t)m0 * kblocks, nrecSA);
+    const __amdgpu_buffer_rsrc_t rSB = rsrc(g.bs + (int64_t)n0 * kblocks, nrecSB);
+
+    // carrier: reference scale per row and the tile's path
+    if constexpr (MODE != 0) {
+        const int ga = min(m0 + tid, g.M - 1), gb = min(n0 + tid, g.N - 1);
+        const bool vec = (kblocks % 16 == 0) && ((((uintptr_t)g.as | (uintptr_t)g.bs) & 15) == 0);
+        int amax, amin, bmax, bmin;
+        row_scale_range(g.as + (int64_t)ga * kblocks, kblocks, vec, amax, amin);
+        row_scale_range(g.bs + (int64_t)gb * kblocks, kblocks, vec, bmax, bmin);
+        sRa[tid] = amax;
+        sRb[tid] = bmax;
+        const bool w = amax - amin > kSpreadMax || bmax - bmin > kSpreadMax || amax == 255 || bmax == 255;
+        const bool wide = __syncthreads_or(w) != 0;
+        if (wide != (MODE == 2)) return;  // uniform across the workgroup
+    }
+
+    // per-lane DMA source offsets, constant along K: lane l of instruction q
+    // fills LDS bytes [16 l, 16 l + 16) of its 1 KiB segment = physical chunk
+    // l % CPR of row seg * (64 / CPR) + l / CPR, i.e. logical chunk pch ^ key
+    int voffA[NIA], voffB[NIB];
+#pragma unroll
+    for (int q = 0; q < NIA; q++) {
+        const int row = (wave * NIA + q) * (64 / CPRA) + lane / CPRA;
+        voffA[q] = row * rowA + (((lane % CPRA) ^ swz_key<RBA>(row)) << 4);
+    }
+#pragma unroll
+    for (int q = 0; q < NIB; q++) {
+        const int row = (wave * NIB + q) * (64 / CPRB) + lane / CPRB;
+        voffB[q] = row * rowB + (((lane % CPRB) ^ swz_key<RBB>(row)) << 4);
+    }
+    const int voffSA = (wave * 64 + lane) * kblocks, voffSB = voffSA;
+
+    auto issue = [&](auto S, int kt) {
+        const bool live = kt < ntk;
+        const int soA = live ? kt * RBA : (int)nrecA, soB = live ? kt * RBB : (int)nrecB;
+        const int soSA = live ? kt * SBY : (int)nrecSA, soSB = live ? kt * SBY : (int)nrecSB;
+#pragma unroll
+        for (int q = 0; q < NIA; q++) dma<16>(rA, stA(S) + (wave * NIA + q) * 1024, voffA[q], soA);
+#pragma unroll
+        for (int q = 0; q < NIB; q++) dma<16>(rB, stB(S) + (wave * NIB + q) * 1024, voffB[q], soB);
+        dma<SBY>(rSA, stSA(S) + wave * 256, voffSA, soSA);
+        dma<SBY>(rSB, stSB(S) + wave * 256, voffSB, soSB);
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    auto compute = [&](auto S) {
+        const uint8_t *tA = stA(S), *tB = stB(S), *tSA = stSA(S), *tSB = stSB(S);
+        if constexpr (MODE == 0) {
+            // scale slot of a row: bytes = blocks 0..3 of the stage; >> 8h leaves
+            // this lane's blocks h and 2 + h at bytes 0 and 2
+            uint32_t sa[4], sbw[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                sa[i] = *reinterpret_cast<const uint32_t *>(&tSA[(wm * 128 + i * 32 + l32) * 4]) >> (8 * h);
+                sbw[i] = *reinterpret_cast<const uint32_t *>(&tSB[(wn * 128 + i * 32 + l32) * 4]) >> (8 * h);
+            }
+            static_for<0, 2>([&](auto step) {
+                constexpr int s = decltype(step)::value;
+                v8i fa[4], fb[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const uint4 t = *reinterpret_cast<const uint4 *>(&tA[swz<RBA>(wm * 128 + i * 32 + l32, 2 * s + h)]);
+                    fa[i] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint4 t = *reinterpret_cast<const uint4 *>(&tB[swz<RBB>(wn * 128 + j * 32 + l32, 2 * s + h)]);
+                    fb[j] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fa[i], fb[j], acc[i][j], 4, 4, 2 * s, (int)sa[i], 2 * s, (int)sbw[j]);
+            });
+        } else if constexpr (MODE == 1) {
+            float sca[4][2], scb[4][2];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int ra_ = wm * 128 + i * 32 + l32, rb_ = wn * 128 + i * 32 + l32;
+                const uint32_t wa = *reinterpret_cast<const uint32_t *>(&tSA[ra_ * 4]);
+                const uint32_t wb = *reinterpret_cast<const uint32_t *>(&tSB[rb_ * 4]);
+                const int Ra = sRa[ra_], Rb = sRb[rb_];
+#pragma unroll
+                for (int q = 0; q < 2; q++) {
+                    sca[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wa >> (8 * q)) & 0xFF) - Ra);
+                    scb[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wb >> (8 * q)) & 0xFF) - Rb);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                v8bf fa[4], fb[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    uint32_t lo, hi;
+                    read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, t, h, lo, hi);
+                    fa[i] = to_bf16x8<FA>(lo, hi, sca[i][t >> 1]);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    uint32_t lo, hi;
+                    read_codes<FB, RBB>(tB, wn * 128 + j * 32 + l32, t, h, lo, hi);
+                    fb[j] = to_bf16x8<FB>(lo, hi, scb[j][t >> 1]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            }
+        } else {
+#pragma unroll 1
+            for (int blk = 0; blk < 2; blk++) {
+                static_for<0, 4>([&](auto ii) {
+                    constexpr int i = decltype(ii)::value;
+                    int sa_r[16];
+#pragma unroll
+                    for (int r = 0; r < 16; r++)
+                        sa_r[r] = tSA[(wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 4 + blk];
+                    static_for<0, 4>([&](auto jj) {
+                        constexpr int j = decltype(jj)::value;
+                        v16f p;
+#pragma unroll
+                        for (int r = 0; r < 16; r++) p[r] = 0.f;
+#pragma unroll
+                        for (int t = 0; t < 2; t++) {
+                            uint32_t lo, hi;
+                            read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, 2 * blk + t, h, lo, hi);
+                            const v8bf a8 = to_bf16x8<FA>(lo, hi, 1.0f);
+                            read_codes<FB, RBB>(tB, wn * 128 + j * 32 + l32, 2 * blk + t, h, lo, hi);
+                            const v8bf b8 = to_bf16x8<FB>(lo, hi, 1.0f);
+                            p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, p, 0, 0, 0);
+                        }
+                        const int sb = tSB[(wn * 128 + j * 32 + l32) * 4 + blk];
+#pragma unroll
+                        for (int r = 0; r < 16; r++) {
+                            const float v = __builtin_amdgcn_ldexpf(p[r], sa_r[r] + sb - 254);
+                            acc[i][j][r] += (sa_r[r] == 255 || sb == 255) ? __builtin_nanf("") : v;
+                        }
+                    });
+                });
+            }
+        }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    issue(I0{}, 0);
+    issue(I1{}, 1);
+    issue(I2{}, 2);
+    for (int kt0 = 0; kt0 < ntk; kt0 += NS) {
+        // stage u holds tile kt0 + u; after the barrier the buffer of the
+        // previous stage is free and receives tile kt0 + u + NS - 1
+        auto body = [&](auto U, auto NEXT) {
+            const int kt = kt0 + decltype(U)::value;
+            wait_vm<LPS * (NS - 2)>();
+            barrier();
+            issue(NEXT, kt + NS - 1);
+            if (kt < ntk) compute(U);
+        };
+        body(I0{}, I3{});
+        body(I1{}, I0{});
+        body(I2{}, I1{});
+        body(I3{}, I2{});
+    }
+    wait_vm<0>();  // drain the out-of-range stage loads before the workgroup ends
+
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int nl = wn * 128 + j * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int ml = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                float v = acc[i][j][r];
+                if constexpr (MODE == 1) v = __builtin_amdgcn_ldexpf(v, sRa[ml] + sRb[nl] - 254);
+                store_c<BF16OUT>(g, m0 + ml, n0 + nl, v);
+            }
+        }
+    }
+}
+
+}  // namespace pipe
+
+// C = 0 for K == 0
+template <bool BF16OUT>
+__global__ void k_zero(void *c, int64_t ldc, int M, int N) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)M * N) return;
+    const int64_t m = i / N, n = i % N;
+    if (BF16OUT)
+        reinterpret_cast<uint16_t *>(c)[m * ldc + n] = 0;
+    else
+        reinterpret_cast<float *>(c)[m * ldc + n] = 0.f;
+}
+
+template <int FA, int FB>
+hipError_t launch_fmt(const GemmArgs &g, bool bf16, hipStream_t stream) {
+    const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(NT);
+    constexpr bool fp4 = FA == E2M1 && FB == E2M1;
+    constexpr int KE = fp4 ? 128 : 64;
+    constexpr int SBY = KE / 32;
+    // pipelined kernels: K a whole number of stages, 16-byte aligned codes,
+    // scale rows aligned for the 2- or 4-byte scale loads, offsets in 32 bits
+    const int64_t rowA = FA == E2M1 ? g.K / 2 : g.K, rowB = FB == E2M1 ? g.K / 2 : g.K;
+    const bool pipelined = g.K % KE == 0 && ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.b % 16 == 0) &&
+                           ((uintptr_t)g.as % SBY == 0) && ((uintptr_t)g.bs % SBY == 0) &&
+                           (int64_t)BM * (rowA > rowB ? rowA : rowB) < ((int64_t)1 << 31);
+    if (pipelined) {
+        if constexpr (fp4) {
+            if (bf16)
+                hipLaunchKernelGGL((pipe::k_gemm_pipe<FA, FB, true, 0>), grid, block, 0, stream, g);
+            else
+                hipLaunchKernelGGL((pipe::k_gemm_pipe<FA, FB, false, 0>), grid, block, 0, stream, g);
+        } else {
+            if (bf16) {
+                hipLaunchKernelGGL((pipe::k_gemm_pipe<FA, FB, true, 1>), grid, block, 0, stream, g);
+                hipLaunchKernelGGL((pipe::k_gemm_pipe<FA, FB, true, 2>), grid, block, 0, stream, g);
+            } else {
+                hipLaunchKernelGGL((pipe::k_gemm_pipe<FA, FB, false, 1>), grid, block, 0, stream, g);
+                hipLaunchKernelGGL((pipe::k_gemm_pipe<FA, FB, false, 2>), grid, block, 0, stream, g);
+            }
+        }
+        return hipGetLastError();
+    }
+    if constexpr (fp4) {
+        if (bf16)
+            hipLaunchKernelGGL((k_gemm_fp4<true>), grid, block, 0, stream, g);
+        else
+            hipLaunchKernelGGL((k_gemm_fp4<false>), grid, block, 0, stream, g);
+    } else {
+        if (bf16) {
+            hipLaunchKernelGGL((k_gemm_carrier<FA, FB, true, false>), grid, block, 0, stream, g);
+            hipLaunchKernelGGL((k_gemm_carrier<FA, FB, true, true>), grid, block, 0, stream, g);
+        } else {
+            hipLaunchKernelGGL((k_gemm_carrier<FA, FB, false, false>), grid, block, 0, stream, g);
+            hipLaunchKernelGGL((k_gemm_carrier<FA, FB, false, true>), grid, block, 0, stream, g);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace mx
