@@ -487,24 +487,34 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_carrier(GemmArgs g) {
 
 
 // ---------------------------------------------------------------------------
-// Pipelined kernels (K a multiple of the stage depth, aligned pointers): the
-// same tiling and arithmetic as above, with operand tiles moved by
-// BUFFER_LOAD ... LDS (global memory straight to LDS, no register staging)
-// through NS = 4 LDS stages, so three K stages are in flight while one is
-// multiplied.  Stage depth: 64 code bytes per row (128 E2M1 or 64 FP8
-// elements; 32 bytes for an E2M1 operand paired with FP8).  Each stage has
-// its own LDS arrays, the loop is unrolled by NS so stage indices are
-// compile-time, and every stage load is issued unconditionally (past the last
-// tile the offset points outside the buffer and the load returns zeros), which
-// keeps the compiler's wait-count tracking exact: a wave waits only for the
-// stage it is about to read.  Rows past M or N also read as zeros through the
-// buffer's range check.
+// Pipelined kernels (K a whole number of stages, aligned pointers): the same
+// tiling and arithmetic as above, restructured for gfx950's memory system.
+//   - Operand tiles move with BUFFER_LOAD ... LDS (global memory straight to
+//     LDS, no register staging).  A stage holds 128 code bytes per row (256
+//     E2M1 or 128 FP8 elements; 64 bytes for an E2M1 operand paired with FP8):
+//     every row request then covers whole 128-byte L2 lines, which measured
+//     twice the L2 throughput of 64-byte slices.  Two stages (2 x 68 KiB of
+//     LDS): one loads while the other is multiplied.
+//   - Each stage has its own LDS arrays and the loop is unrolled by the stage
+//     count, so stage indices are compile-time; every stage load is issued
+//     unconditionally (past the last tile its offset points outside the
+//     buffer and the load returns zeros).  This keeps the compiler's
+//     wait-count tracking exact, and rows past M or N read as zeros through
+//     the buffer's range check.
+//   - The matrix instructions run with B as the first operand, so a lane's
+//     accumulators hold four consecutive columns of one row of C.  The
+//     epilogue stages each wave's 128 x 128 tile of C through the (then idle)
+//     LDS stage buffers and writes whole 256-byte row segments.
 namespace pipe {
 
 typedef __attribute__((address_space(3))) void *lds_t;
-constexpr int NS = 4;
+constexpr int NS = 2;
 
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Workgroup barrier without the compiler's implied vmcnt(0): the stage loads
+// are waited for explicitly.  LDS reads this wave issued before the barrier
+// are drained first (lgkmcnt(0)): the compiler may leave them in flight past
+// an inline-asm barrier, after which other waves' DMA may overwrite the buffer.
+__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -519,8 +529,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
 template <int SZ>
 __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, void *lds, int voff, int soff) {
     if constexpr (SZ == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)lds, 16, voff, soff, 0, 0);
-    else if constexpr (SZ == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)lds, 4, voff, soff, 0, 0);
-    else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)lds, 2, voff, soff, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)lds, 4, voff, soff, 0, 0);
 }
 
 // max and min of a row's E8M0 bytes (uint4 loads when aligned)
@@ -546,46 +555,59 @@ __device__ __forceinline__ void row_scale_range(const uint8_t *p, int n, bool ve
     }
 }
 
+// four consecutive columns n .. n+3 of row m
+template <bool BF16OUT>
+__device__ __forceinline__ void store_c4(const GemmArgs &g, int m, int n, float v0, float v1, float v2, float v3,
+                                         bool vec) {
+    if (m >= g.M) return;
+    if (vec && n + 3 < g.N) {
+        if constexpr (BF16OUT) {
+            const uint32_t lo = bf16_rne(v0) | (bf16_rne(v1) << 16), hi = bf16_rne(v2) | (bf16_rne(v3) << 16);
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(g.c) + (int64_t)m * g.ldc + n) = make_uint2(lo, hi);
+        } else {
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(g.c) + (int64_t)m * g.ldc + n) =
+                make_float4(v0, v1, v2, v3);
+        }
+    } else {
+        store_c<BF16OUT>(g, m, n, v0);
+        store_c<BF16OUT>(g, m, n + 1, v1);
+        store_c<BF16OUT>(g, m, n + 2, v2);
+        store_c<BF16OUT>(g, m, n + 3, v3);
+    }
+}
+
 // MODE 0: E2M1 x E2M1, block-scaled instruction.  MODE 1: carrier fast path.
 // MODE 2: carrier exact per-block path (tiles the fast path leaves).
+// 512 threads: 8 waves, two per SIMD, each a 128 x 64 tile of C (4 x 2 tiles
+// of 32 x 32, 128 accumulators), so one wave multiplies while the other
+// waits on LDS, the barrier or the stage loads.
+constexpr int PNT = 512;
 template <int FA, int FB, bool BF16OUT, int MODE>
-__global__ __launch_bounds__(NT, 1) void k_gemm_pipe(GemmArgs g) {
+__global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     constexpr bool A4 = FA == E2M1, B4 = FB == E2M1;
-    constexpr int KE = (A4 && B4) ? 128 : 64;          // K elements per stage
+    constexpr int KE = (A4 && B4) ? 256 : 128;         // K elements per stage
     constexpr int RBA = A4 ? KE / 2 : KE, RBB = B4 ? KE / 2 : KE;
-    constexpr int SBY = KE / 32;                       // scale bytes per row per stage
-    constexpr int NIA = BM * RBA / 1024 / 4, NIB = BN * RBB / 1024 / 4;  // 1 KiB DMA per wave instruction
-    constexpr int LPS = NIA + NIB + 2;                 // DMA instructions per wave per stage
+    constexpr int SBY = KE / 32;                       // scale bytes per row per stage: 8 or 4
+    constexpr int NSW = SBY / 4;                       // scale words per row per stage
+    constexpr int NW = PNT / 64;                       // waves
+    constexpr int NIA = BM * RBA / 1024 / NW, NIB = BN * RBB / 1024 / NW;  // 1 KiB DMA per wave instruction
+    constexpr int NIS = 2 * NSW * 4 / NW;              // 64-row scale DMAs per wave (A and B words)
     constexpr int CPRA = RBA / 16, CPRB = RBB / 16;
+    static_assert(NIA >= 1 && NIB >= 1 && NIS >= 1, "DMA split");
 
-    __shared__ __attribute__((aligned(16))) uint8_t sA0[BM * RBA], sA1[BM * RBA], sA2[BM * RBA], sA3[BM * RBA];
-    __shared__ __attribute__((aligned(16))) uint8_t sB0[BN * RBB], sB1[BN * RBB], sB2[BN * RBB], sB3[BN * RBB];
-    __shared__ __attribute__((aligned(16))) uint8_t sSA0[BM * 4], sSA1[BM * 4], sSA2[BM * 4], sSA3[BM * 4];
-    __shared__ __attribute__((aligned(16))) uint8_t sSB0[BN * 4], sSB1[BN * 4], sSB2[BN * 4], sSB3[BN * 4];
+    __shared__ __attribute__((aligned(16))) uint8_t sA0[BM * RBA], sA1[BM * RBA];
+    __shared__ __attribute__((aligned(16))) uint8_t sB0[BN * RBB], sB1[BN * RBB];
+    __shared__ __attribute__((aligned(16))) uint8_t sS0[2 * NSW][BM * 4], sS1[2 * NSW][BM * 4];  // [A words, B words]
     __shared__ int sRa[BM], sRb[BN];
-    auto stA = [&](auto S) -> uint8_t * {
-        constexpr int s = decltype(S)::value;
-        if constexpr (s == 0) return sA0; else if constexpr (s == 1) return sA1;
-        else if constexpr (s == 2) return sA2; else return sA3;
-    };
-    auto stB = [&](auto S) -> uint8_t * {
-        constexpr int s = decltype(S)::value;
-        if constexpr (s == 0) return sB0; else if constexpr (s == 1) return sB1;
-        else if constexpr (s == 2) return sB2; else return sB3;
-    };
-    auto stSA = [&](auto S) -> uint8_t * {
-        constexpr int s = decltype(S)::value;
-        if constexpr (s == 0) return sSA0; else if constexpr (s == 1) return sSA1;
-        else if constexpr (s == 2) return sSA2; else return sSA3;
-    };
-    auto stSB = [&](auto S) -> uint8_t * {
-        constexpr int s = decltype(S)::value;
-        if constexpr (s == 0) return sSB0; else if constexpr (s == 1) return sSB1;
-        else if constexpr (s == 2) return sSB2; else return sSB3;
+    auto stA = [&](auto S) -> uint8_t * { if constexpr (decltype(S)::value == 0) return sA0; else return sA1; };
+    auto stB = [&](auto S) -> uint8_t * { if constexpr (decltype(S)::value == 0) return sB0; else return sB1; };
+    auto stS = [&](auto S, int a) -> uint8_t * {  // a < NSW: A word a; a >= NSW: B word a - NSW
+        if constexpr (decltype(S)::value == 0) return sS0[a]; else return sS1[a];
     };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases go through M0
+    const int wm = wave >> 2, wn = wave & 3;  // wave tile: rows wm*128 .. +127, cols wn*64 .. +63
     const int l32 = lane & 31, h = lane >> 5;
     int m0, n0;
     tile_of(g, m0, n0);
@@ -601,104 +623,120 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_pipe(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t rSA = rsrc(g.as + (int64_t)m0 * kblocks, nrecSA);
     const __amdgpu_buffer_rsrc_t rSB = rsrc(g.bs + (int64_t)n0 * kblocks, nrecSB);
 
-    // carrier: reference scale per row and the tile's path
+    // carrier: reference scale per row and the tile's path (threads 0..255:
+    // rows of A, 256..511: rows of B)
     if constexpr (MODE != 0) {
-        const int ga = min(m0 + tid, g.M - 1), gb = min(n0 + tid, g.N - 1);
+        const bool isA = tid < BM;
+        const int r = isA ? tid : tid - BM;
+        const int gr = isA ? min(m0 + r, g.M - 1) : min(n0 + r, g.N - 1);
         const bool vec = (kblocks % 16 == 0) && ((((uintptr_t)g.as | (uintptr_t)g.bs) & 15) == 0);
-        int amax, amin, bmax, bmin;
-        row_scale_range(g.as + (int64_t)ga * kblocks, kblocks, vec, amax, amin);
-        row_scale_range(g.bs + (int64_t)gb * kblocks, kblocks, vec, bmax, bmin);
-        sRa[tid] = amax;
-        sRb[tid] = bmax;
-        const bool w = amax - amin > kSpreadMax || bmax - bmin > kSpreadMax || amax == 255 || bmax == 255;
+        int mx_, mn_;
+        row_scale_range((isA ? g.as : g.bs) + (int64_t)gr * kblocks, kblocks, vec, mx_, mn_);
+        (isA ? sRa : sRb)[r] = mx_;
+        const bool w = mx_ - mn_ > kSpreadMax || mx_ == 255;
         const bool wide = __syncthreads_or(w) != 0;
         if (wide != (MODE == 2)) return;  // uniform across the workgroup
     }
 
     // per-lane DMA source offsets, constant along K: lane l of instruction q
     // fills LDS bytes [16 l, 16 l + 16) of its 1 KiB segment = physical chunk
-    // l % CPR of row seg * (64 / CPR) + l / CPR, i.e. logical chunk pch ^ key
-    int voffA[NIA], voffB[NIB];
-#pragma unroll
-    for (int q = 0; q < NIA; q++) {
-        const int row = (wave * NIA + q) * (64 / CPRA) + lane / CPRA;
-        voffA[q] = row * rowA + (((lane % CPRA) ^ swz_key<RBA>(row)) << 4);
-    }
-#pragma unroll
-    for (int q = 0; q < NIB; q++) {
-        const int row = (wave * NIB + q) * (64 / CPRB) + lane / CPRB;
-        voffB[q] = row * rowB + (((lane % CPRB) ^ swz_key<RBB>(row)) << 4);
-    }
-    const int voffSA = (wave * 64 + lane) * kblocks, voffSB = voffSA;
+    // l % CPR of row seg * (64 / CPR) + l / CPR, i.e. logical chunk pch ^ key.
+    // Instruction q's rows are instruction 0's plus q * 64 / CPR, which leaves
+    // the swizzle key unchanged, so the per-q part is a uniform (scalar) offset.
+    static_assert(64 / CPRA >= 8 && 64 / CPRB >= 8, "row step keeps the swizzle key");
+    const int rowA0 = wave * NIA * (64 / CPRA) + lane / CPRA, rowB0 = wave * NIB * (64 / CPRB) + lane / CPRB;
+    const int voffA = rowA0 * rowA + (((lane % CPRA) ^ swz_key<RBA>(rowA0)) << 4);
+    const int voffB = rowB0 * rowB + (((lane % CPRB) ^ swz_key<RBB>(rowB0)) << 4);
 
     auto issue = [&](auto S, int kt) {
         const bool live = kt < ntk;
         const int soA = live ? kt * RBA : (int)nrecA, soB = live ? kt * RBB : (int)nrecB;
-        const int soSA = live ? kt * SBY : (int)nrecSA, soSB = live ? kt * SBY : (int)nrecSB;
 #pragma unroll
-        for (int q = 0; q < NIA; q++) dma<16>(rA, stA(S) + (wave * NIA + q) * 1024, voffA[q], soA);
+        for (int q = 0; q < NIA; q++)
+            dma<16>(rA, stA(S) + (wave * NIA + q) * 1024, voffA, soA + q * (64 / CPRA) * rowA);
 #pragma unroll
-        for (int q = 0; q < NIB; q++) dma<16>(rB, stB(S) + (wave * NIB + q) * 1024, voffB[q], soB);
-        dma<SBY>(rSA, stSA(S) + wave * 256, voffSA, soSA);
-        dma<SBY>(rSB, stSB(S) + wave * 256, voffSB, soSB);
+        for (int q = 0; q < NIB; q++)
+            dma<16>(rB, stB(S) + (wave * NIB + q) * 1024, voffB, soB + q * (64 / CPRB) * rowB);
+        // scale words: 2 * NSW arrays of 256 rows, 64 rows per instruction
+#pragma unroll
+        for (int u = 0; u < NIS; u++) {
+            const int t = wave * NIS + u;          // instruction index
+            const int a = t / 4, rows0 = (t % 4) * 64;
+            const bool isA = a < NSW;
+            const int w = isA ? a : a - NSW;
+            const int voff = (rows0 + lane) * kblocks;
+            if (isA)
+                dma<4>(rSA, stS(S, a) + rows0 * 4, voff, live ? kt * SBY + 4 * w : (int)nrecSA);
+            else
+                dma<4>(rSB, stS(S, a) + rows0 * 4, voff, live ? kt * SBY + 4 * w : (int)nrecSB);
+        }
     };
 
-    v16f acc[4][4];
+    v16f acc[4][2];  // acc[i][j]: C^T tile of A rows i, B rows j
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
     auto compute = [&](auto S) {
-        const uint8_t *tA = stA(S), *tB = stB(S), *tSA = stSA(S), *tSB = stSB(S);
+        const uint8_t *tA = stA(S), *tB = stB(S);
         if constexpr (MODE == 0) {
-            // scale slot of a row: bytes = blocks 0..3 of the stage; >> 8h leaves
-            // this lane's blocks h and 2 + h at bytes 0 and 2
-            uint32_t sa[4], sbw[4];
+            // scale words of a row: blocks 4w .. 4w+3 of the stage; >> 8h leaves
+            // this lane's blocks 4w + h and 4w + 2 + h at bytes 0 and 2
+            uint32_t sa[4][NSW], sbw[2][NSW];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                sa[i] = *reinterpret_cast<const uint32_t *>(&tSA[(wm * 128 + i * 32 + l32) * 4]) >> (8 * h);
-                sbw[i] = *reinterpret_cast<const uint32_t *>(&tSB[(wn * 128 + i * 32 + l32) * 4]) >> (8 * h);
+            for (int w = 0; w < NSW; w++) {
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    sa[i][w] = *reinterpret_cast<const uint32_t *>(&stS(S, w)[(wm * 128 + i * 32 + l32) * 4]) >> (8 * h);
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    sbw[j][w] = *reinterpret_cast<const uint32_t *>(&stS(S, NSW + w)[(wn * 64 + j * 32 + l32) * 4]) >> (8 * h);
             }
-            static_for<0, 2>([&](auto step) {
+            static_for<0, KE / 64>([&](auto step) {
                 constexpr int s = decltype(step)::value;
-                v8i fa[4], fb[4];
+                constexpr int w = s / 2, sel = (2 * s) % 4;
+                v8i fa[4], fb[2];
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const uint4 t = *reinterpret_cast<const uint4 *>(&tA[swz<RBA>(wm * 128 + i * 32 + l32, 2 * s + h)]);
                     fa[i] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
                 }
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const uint4 t = *reinterpret_cast<const uint4 *>(&tB[swz<RBB>(wn * 128 + j * 32 + l32, 2 * s + h)]);
+                for (int j = 0; j < 2; j++) {
+                    const uint4 t = *reinterpret_cast<const uint4 *>(&tB[swz<RBB>(wn * 64 + j * 32 + l32, 2 * s + h)]);
                     fb[j] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
                 }
 #pragma unroll
                 for (int i = 0; i < 4; i++)
 #pragma unroll
-                    for (int j = 0; j < 4; j++)
+                    for (int j = 0; j < 2; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fa[i], fb[j], acc[i][j], 4, 4, 2 * s, (int)sa[i], 2 * s, (int)sbw[j]);
+                            fb[j], fa[i], acc[i][j], 4, 4, sel, (int)sbw[j][w], sel, (int)sa[i][w]);
             });
         } else if constexpr (MODE == 1) {
-            float sca[4][2], scb[4][2];
+            float sca[4][4], scb[2][4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int ra_ = wm * 128 + i * 32 + l32, rb_ = wn * 128 + i * 32 + l32;
-                const uint32_t wa = *reinterpret_cast<const uint32_t *>(&tSA[ra_ * 4]);
-                const uint32_t wb = *reinterpret_cast<const uint32_t *>(&tSB[rb_ * 4]);
-                const int Ra = sRa[ra_], Rb = sRb[rb_];
+                const int ra_ = wm * 128 + i * 32 + l32;
+                const uint32_t wa = *reinterpret_cast<const uint32_t *>(&stS(S, 0)[ra_ * 4]);
+                const int Ra = sRa[ra_];
 #pragma unroll
-                for (int q = 0; q < 2; q++) {
-                    sca[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wa >> (8 * q)) & 0xFF) - Ra);
-                    scb[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wb >> (8 * q)) & 0xFF) - Rb);
-                }
+                for (int q = 0; q < 4; q++) sca[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wa >> (8 * q)) & 0xFF) - Ra);
             }
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
-                v8bf fa[4], fb[4];
+            for (int j = 0; j < 2; j++) {
+                const int rb_ = wn * 64 + j * 32 + l32;
+                const uint32_t wb = *reinterpret_cast<const uint32_t *>(&stS(S, 1)[rb_ * 4]);
+                const int Rb = sRb[rb_];
+#pragma unroll
+                for (int q = 0; q < 4; q++) scb[j][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wb >> (8 * q)) & 0xFF) - Rb);
+            }
+#pragma unroll
+            for (int t = 0; t < KE / 16; t++) {
+                v8bf fa[4], fb[2];
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     uint32_t lo, hi;
@@ -706,28 +744,28 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_pipe(GemmArgs g) {
                     fa[i] = to_bf16x8<FA>(lo, hi, sca[i][t >> 1]);
                 }
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
+                for (int j = 0; j < 2; j++) {
                     uint32_t lo, hi;
-                    read_codes<FB, RBB>(tB, wn * 128 + j * 32 + l32, t, h, lo, hi);
+                    read_codes<FB, RBB>(tB, wn * 64 + j * 32 + l32, t, h, lo, hi);
                     fb[j] = to_bf16x8<FB>(lo, hi, scb[j][t >> 1]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; i++)
 #pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < 2; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
             }
         } else {
 #pragma unroll 1
-            for (int blk = 0; blk < 2; blk++) {
-                static_for<0, 4>([&](auto ii) {
-                    constexpr int i = decltype(ii)::value;
-                    int sa_r[16];
+            for (int blk = 0; blk < KE / 32; blk++) {
+                static_for<0, 2>([&](auto jj) {
+                    constexpr int j = decltype(jj)::value;
+                    int sb_r[16];  // scale of column n = 8(r/4) + 4h + r%4 of tile j
 #pragma unroll
                     for (int r = 0; r < 16; r++)
-                        sa_r[r] = tSA[(wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 4 + blk];
-                    static_for<0, 4>([&](auto jj) {
-                        constexpr int j = decltype(jj)::value;
+                        sb_r[r] = stS(S, 1)[(wn * 64 + j * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 4 + blk];
+                    static_for<0, 4>([&](auto ii) {
+                        constexpr int i = decltype(ii)::value;
                         v16f p;
 #pragma unroll
                         for (int r = 0; r < 16; r++) p[r] = 0.f;
@@ -736,15 +774,15 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_pipe(GemmArgs g) {
                             uint32_t lo, hi;
                             read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, 2 * blk + t, h, lo, hi);
                             const v8bf a8 = to_bf16x8<FA>(lo, hi, 1.0f);
-                            read_codes<FB, RBB>(tB, wn * 128 + j * 32 + l32, 2 * blk + t, h, lo, hi);
+                            read_codes<FB, RBB>(tB, wn * 64 + j * 32 + l32, 2 * blk + t, h, lo, hi);
                             const v8bf b8 = to_bf16x8<FB>(lo, hi, 1.0f);
-                            p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, p, 0, 0, 0);
+                            p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8, a8, p, 0, 0, 0);
                         }
-                        const int sb = tSB[(wn * 128 + j * 32 + l32) * 4 + blk];
+                        const int sa = stS(S, 0)[(wm * 128 + i * 32 + l32) * 4 + blk];
 #pragma unroll
                         for (int r = 0; r < 16; r++) {
-                            const float v = __builtin_amdgcn_ldexpf(p[r], sa_r[r] + sb - 254);
-                            acc[i][j][r] += (sa_r[r] == 255 || sb == 255) ? __builtin_nanf("") : v;
+                            const float v = __builtin_amdgcn_ldexpf(p[r], sa + sb_r[r] - 254);
+                            acc[i][j][r] += (sa == 255 || sb_r[r] == 255) ? __builtin_nanf("") : v;
                         }
                     });
                 });
@@ -754,41 +792,103 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_pipe(GemmArgs g) {
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
     issue(I0{}, 0);
-    issue(I1{}, 1);
-    issue(I2{}, 2);
     for (int kt0 = 0; kt0 < ntk; kt0 += NS) {
-        // stage u holds tile kt0 + u; after the barrier the buffer of the
-        // previous stage is free and receives tile kt0 + u + NS - 1
+        // stage u holds tile kt0 + u; after the barrier the other stage's
+        // buffer is free and receives the next tile
         auto body = [&](auto U, auto NEXT) {
             const int kt = kt0 + decltype(U)::value;
-            wait_vm<LPS * (NS - 2)>();
+            wait_vm<0>();
             barrier();
-            issue(NEXT, kt + NS - 1);
+            issue(NEXT, kt + 1);
             if (kt < ntk) compute(U);
         };
-        body(I0{}, I3{});
+        body(I0{}, I1{});
         body(I1{}, I0{});
-        body(I2{}, I1{});
-        body(I3{}, I2{});
     }
     wait_vm<0>();  // drain the out-of-range stage loads before the workgroup ends
 
+    // lane: row m = i*32 + l32 of the wave's tile, columns 8(r/4) + 4h + r%4 of tile j
+    auto value = [&](int i, int j, int q, int e) -> float {
+        float v = acc[i][j][4 * q + e];
+        if constexpr (MODE == 1) v = __builtin_amdgcn_ldexpf(v, sRa[wm * 128 + i * 32 + l32] +
+                                                                  sRb[wn * 64 + j * 32 + 8 * q + 4 * h + e] - 254);
+        return v;
+    };
+    if constexpr (RBA == 128 && RBB == 128) {
+        // Stage the wave's 128 x 64 tile of C through LDS (16 KiB per wave in
+        // the stage buffers, free once every wave has left the main loop) and
+        // write it back with consecutive lanes covering whole 128-byte (bf16)
+        // or 256-byte (fp32) row segments.  16-byte chunks are XOR-swizzled by
+        // the row so the column-wise writes spread over the banks.  fp32 output
+        // goes in two passes of 64 rows.
+        barrier();
+        uint8_t *reg = ((wave >> 1) == 0 ? sA0 : (wave >> 1) == 1 ? sA1 : (wave >> 1) == 2 ? sB0 : sB1) + (wave & 1) * 16384;
+        constexpr int ESZ = BF16OUT ? 2 : 4;
+        constexpr int ROWB = 64 * ESZ;             // bytes per row of the wave's tile
+        constexpr int CPR = ROWB / 16;             // 16-byte chunks per row: 8 or 16
+        constexpr int PASS_ROWS = 16384 / ROWB;    // rows per pass: 128 or 64
+        constexpr int PASSES = 128 / PASS_ROWS;
+        const int mbase = m0 + wm * 128, nbase = n0 + wn * 64;
+        const bool full_cols = nbase + 64 <= g.N;
+        const bool vec = full_cols && (g.ldc % (16 / ESZ) == 0) && (((uintptr_t)g.c & 15) == 0);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+        for (int pass = 0; pass < PASSES; pass++) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int nl = wn * 128 + j * 32 + l32;
+            for (int ii = 0; ii < 4 / PASSES; ii++) {
+                const int i = pass * (4 / PASSES) + ii;
+                const int m = ii * 32 + l32;  // row within the pass
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int ml = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                float v = acc[i][j][r];
-                if constexpr (MODE == 1) v = __builtin_amdgcn_ldexpf(v, sRa[ml] + sRb[nl] - 254);
-                store_c<BF16OUT>(g, m0 + ml, n0 + nl, v);
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const float v0 = value(i, j, q, 0), v1 = value(i, j, q, 1);
+                        const float v2 = value(i, j, q, 2), v3 = value(i, j, q, 3);
+                        if constexpr (BF16OUT) {
+                            const int c = 4 * j + q;  // 8-byte half h of 16-byte chunk c
+                            const int off = m * ROWB + ((c ^ (m & (CPR - 1))) << 4) + 8 * h;
+                            *reinterpret_cast<uint2 *>(&reg[off]) =
+                                make_uint2(bf16_rne(v0) | (bf16_rne(v1) << 16), bf16_rne(v2) | (bf16_rne(v3) << 16));
+                        } else {
+                            const int c = 8 * j + 2 * q + h;
+                            const int off = m * ROWB + ((c ^ (m & (CPR - 1))) << 4);
+                            *reinterpret_cast<float4 *>(&reg[off]) = make_float4(v0, v1, v2, v3);
+                        }
+                    }
+            }
+            // read back row-contiguous: lane -> row lane / CPR (+ 64 / CPR per step), chunk lane % CPR
+#pragma unroll
+            for (int step = 0; step < PASS_ROWS * CPR / 64; step++) {
+                const int m = step * (64 / CPR) + lane / CPR, c = lane % CPR;
+                const uint4 t = *reinterpret_cast<const uint4 *>(&reg[m * ROWB + ((c ^ (m & (CPR - 1))) << 4)]);
+                const int gm = mbase + pass * PASS_ROWS + m, gn = nbase + c * (16 / ESZ);
+                if (gm >= g.M) continue;
+                if (vec) {
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(g.c) + ((int64_t)gm * g.ldc + gn) * ESZ) = t;
+                } else {
+                    const uint32_t w4[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+                    for (int e = 0; e < 16 / ESZ; e++) {
+                        if (gn + e >= g.N) break;
+                        if constexpr (BF16OUT)
+                            reinterpret_cast<uint16_t *>(g.c)[(int64_t)gm * g.ldc + gn + e] =
+                                (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                        else
+                            reinterpret_cast<uint32_t *>(g.c)[(int64_t)gm * g.ldc + gn + e] = w4[e];
+                    }
+                }
             }
         }
+    } else {
+        const bool vec = (g.ldc % 4 == 0) && (((uintptr_t)g.c & (BF16OUT ? 7 : 15)) == 0);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    store_c4<BF16OUT>(g, m0 + wm * 128 + i * 32 + l32, n0 + wn * 64 + j * 32 + 8 * q + 4 * h,
+                                      value(i, j, q, 0), value(i, j, q, 1), value(i, j, q, 2), value(i, j, q, 3), vec);
     }
 }
 
@@ -810,15 +910,15 @@ template <int FA, int FB>
 hipError_t launch_fmt(const GemmArgs &g, bool bf16, hipStream_t stream) {
     const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(NT);
     constexpr bool fp4 = FA == E2M1 && FB == E2M1;
-    constexpr int KE = fp4 ? 128 : 64;
-    constexpr int SBY = KE / 32;
+    constexpr int KE = fp4 ? 256 : 128;
     // pipelined kernels: K a whole number of stages, 16-byte aligned codes,
     // scale rows aligned for the 2- or 4-byte scale loads, offsets in 32 bits
     const int64_t rowA = FA == E2M1 ? g.K / 2 : g.K, rowB = FB == E2M1 ? g.K / 2 : g.K;
     const bool pipelined = g.K % KE == 0 && ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.b % 16 == 0) &&
-                           ((uintptr_t)g.as % SBY == 0) && ((uintptr_t)g.bs % SBY == 0) &&
+                           ((uintptr_t)g.as % 4 == 0) && ((uintptr_t)g.bs % 4 == 0) &&
                            (int64_t)BM * (rowA > rowB ? rowA : rowB) < ((int64_t)1 << 31);
     if (pipelined) {
+        const dim3 block(pipe::PNT);
         if constexpr (fp4) {
             if (bf16)
                 hipLaunchKernelGGL((pipe::k_gemm_pipe<FA, FB, true, 0>), grid, block, 0, stream, g);
