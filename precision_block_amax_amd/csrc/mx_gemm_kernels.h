@@ -514,7 +514,13 @@ constexpr int NS = 2;
 // are waited for explicitly.  LDS reads this wave issued before the barrier
 // are drained first (lgkmcnt(0)): the compiler may leave them in flight past
 // an inline-asm barrier, after which other waves' DMA may overwrite the buffer.
-__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The scheduling fences keep register-only work (MFMAs) on its side of the
+// barrier, so one stage's fragments are never live across it.
+__device__ __forceinline__ void barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -522,14 +528,26 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+// Raw buffer descriptor: base address, no stride, `bytes` records (reads at
+// or past the end return zeros), dword data format.
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
 }
 
-template <int SZ>
-__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, void *lds, int voff, int soff) {
-    if constexpr (SZ == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)lds, 16, voff, soff, 0, 0);
-    else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)lds, 4, voff, soff, 0, 0);
+// 16 bytes per lane from buffer r at voff + soff straight into LDS: lane l
+// lands at lds + 16 l.  Written as inline asm so that the compiler's own
+// wait-count tracking, which cannot always tell the stage buffers apart and
+// would then wait for every load in flight before an LDS read, stays out of
+// it: the kernel waits for the loads explicitly (vmcnt) before its barriers.
+// M0 carries the LDS address and needs one wait state before the load.
+__device__ __forceinline__ void dma16(v4i r, void *lds, int voff, int soff) {
+    const uint32_t m = (uint32_t)(uintptr_t)(lds_t)lds;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+                 :
+                 : "v"(voff), "s"(m), "s"(r), "s"(soff)
+                 : "memory", "m0");
 }
 
 // max and min of a row's E8M0 bytes (uint4 loads when aligned)
@@ -589,21 +607,24 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     constexpr int RBA = A4 ? KE / 2 : KE, RBB = B4 ? KE / 2 : KE;
     constexpr int SBY = KE / 32;                       // scale bytes per row per stage: 8 or 4
     constexpr int NSW = SBY / 4;                       // scale words per row per stage
+    constexpr int SPS = 16 / SBY;                      // stages per scale slot (16 scale bytes per row)
     constexpr int NW = PNT / 64;                       // waves
     constexpr int NIA = BM * RBA / 1024 / NW, NIB = BN * RBB / 1024 / NW;  // 1 KiB DMA per wave instruction
-    constexpr int NIS = 2 * NSW * 4 / NW;              // 64-row scale DMAs per wave (A and B words)
     constexpr int CPRA = RBA / 16, CPRB = RBB / 16;
-    static_assert(NIA >= 1 && NIB >= 1 && NIS >= 1, "DMA split");
+    static_assert(NIA >= 1 && NIB >= 1, "DMA split");
+    static_assert(NW == 8 && BM == 256 && BN == 256, "one 64-row scale DMA per wave");
 
+    // Code stages alternate between two buffers; scale slots (16 bytes per
+    // row: the scales of SPS consecutive stages) alternate between two more.
+    // Every buffer is a separate LDS object selected at compile time, so the
+    // compiler can see that a stage load never aliases the buffer being read.
     __shared__ __attribute__((aligned(16))) uint8_t sA0[BM * RBA], sA1[BM * RBA];
     __shared__ __attribute__((aligned(16))) uint8_t sB0[BN * RBB], sB1[BN * RBB];
-    __shared__ __attribute__((aligned(16))) uint8_t sS0[2 * NSW][BM * 4], sS1[2 * NSW][BM * 4];  // [A words, B words]
+    __shared__ __attribute__((aligned(16))) uint8_t sS0[2][BM * 16], sS1[2][BM * 16];  // [A, B][row * 16 + byte]
     __shared__ int sRa[BM], sRb[BN];
     auto stA = [&](auto S) -> uint8_t * { if constexpr (decltype(S)::value == 0) return sA0; else return sA1; };
     auto stB = [&](auto S) -> uint8_t * { if constexpr (decltype(S)::value == 0) return sB0; else return sB1; };
-    auto stS = [&](auto S, int a) -> uint8_t * {  // a < NSW: A word a; a >= NSW: B word a - NSW
-        if constexpr (decltype(S)::value == 0) return sS0[a]; else return sS1[a];
-    };
+    auto stS = [&](auto T, int op) -> uint8_t * { if constexpr (decltype(T)::value == 0) return sS0[op]; else return sS1[op]; };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases go through M0
@@ -618,10 +639,10 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     const int mrows = min(BM, g.M - m0), nrows = min(BN, g.N - n0);
     const uint32_t nrecA = (uint32_t)mrows * rowA, nrecB = (uint32_t)nrows * rowB;
     const uint32_t nrecSA = (uint32_t)mrows * kblocks, nrecSB = (uint32_t)nrows * kblocks;
-    const __amdgpu_buffer_rsrc_t rA = rsrc(g.a + (int64_t)m0 * rowA, nrecA);
-    const __amdgpu_buffer_rsrc_t rB = rsrc(g.b + (int64_t)n0 * rowB, nrecB);
-    const __amdgpu_buffer_rsrc_t rSA = rsrc(g.as + (int64_t)m0 * kblocks, nrecSA);
-    const __amdgpu_buffer_rsrc_t rSB = rsrc(g.bs + (int64_t)n0 * kblocks, nrecSB);
+    const v4i rA = rsrc(g.a + (int64_t)m0 * rowA, nrecA);
+    const v4i rB = rsrc(g.b + (int64_t)n0 * rowB, nrecB);
+    const v4i rSA = rsrc(g.as + (int64_t)m0 * kblocks, nrecSA);
+    const v4i rSB = rsrc(g.bs + (int64_t)n0 * kblocks, nrecSB);
 
     // carrier: reference scale per row and the tile's path (threads 0..255:
     // rows of A, 256..511: rows of B)
@@ -648,28 +669,28 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     const int voffA = rowA0 * rowA + (((lane % CPRA) ^ swz_key<RBA>(rowA0)) << 4);
     const int voffB = rowB0 * rowB + (((lane % CPRB) ^ swz_key<RBB>(rowB0)) << 4);
 
-    auto issue = [&](auto S, int kt) {
+    // scale slot loads: wave w fetches 16 bytes of each of the 64 rows
+    // 64 (w % 4) .. +63 of operand w / 4 (A, then B); one line per row
+    const int sop = wave >> 2, srow0 = (wave & 3) * 64;
+    const int svoff = (srow0 + lane) * kblocks;
+
+    // codes of stage kt into code buffer S; with SCALES, also the scales of
+    // stages kt .. kt + SPS - 1 into scale slot T.  Past the last stage the
+    // offsets point beyond the buffers' records, which reads zeros.
+    auto issue = [&](auto S, auto T, auto SCALES, int kt) {
         const bool live = kt < ntk;
         const int soA = live ? kt * RBA : (int)nrecA, soB = live ? kt * RBB : (int)nrecB;
 #pragma unroll
         for (int q = 0; q < NIA; q++)
-            dma<16>(rA, stA(S) + (wave * NIA + q) * 1024, voffA, soA + q * (64 / CPRA) * rowA);
+            dma16(rA, stA(S) + (wave * NIA + q) * 1024, voffA, soA + q * (64 / CPRA) * rowA);
 #pragma unroll
         for (int q = 0; q < NIB; q++)
-            dma<16>(rB, stB(S) + (wave * NIB + q) * 1024, voffB, soB + q * (64 / CPRB) * rowB);
-        // scale words: 2 * NSW arrays of 256 rows, 64 rows per instruction
-#pragma unroll
-        for (int u = 0; u < NIS; u++) {
-            const int t = wave * NIS + u;          // instruction index
-            const int a = t / 4, rows0 = (t % 4) * 64;
-            const bool isA = a < NSW;
-            const int w = isA ? a : a - NSW;
-            const int voff = (rows0 + lane) * kblocks;
-            if (isA)
-                dma<4>(rSA, stS(S, a) + rows0 * 4, voff, live ? kt * SBY + 4 * w : (int)nrecSA);
-            else
-                dma<4>(rSB, stS(S, a) + rows0 * 4, voff, live ? kt * SBY + 4 * w : (int)nrecSB);
-        }
+            dma16(rB, stB(S) + (wave * NIB + q) * 1024, voffB, soB + q * (64 / CPRB) * rowB);
+        // branch-free (uniform selects): a branch would split the loop body
+        // into blocks, and the compiler would then sink each stage's MFMAs
+        // into the block of their next use, past the barrier
+        if constexpr (decltype(SCALES)::value)
+            dma16(sop ? rSB : rSA, stS(T, sop) + srow0 * 16, svoff, live ? kt * SBY : (int)(sop ? nrecSB : nrecSA));
     };
 
     v16f acc[4][2];  // acc[i][j]: C^T tile of A rows i, B rows j
@@ -680,8 +701,10 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    auto compute = [&](auto S) {
+    // stage held in code buffer S whose scales are bytes SBY * P .. of slot T
+    auto compute = [&](auto S, auto T, auto P) {
         const uint8_t *tA = stA(S), *tB = stB(S);
+        const uint8_t *tSA = stS(T, 0) + SBY * decltype(P)::value, *tSB = stS(T, 1) + SBY * decltype(P)::value;
         if constexpr (MODE == 0) {
             // scale words of a row: blocks 4w .. 4w+3 of the stage; >> 8h leaves
             // this lane's blocks 4w + h and 4w + 2 + h at bytes 0 and 2
@@ -690,38 +713,47 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
             for (int w = 0; w < NSW; w++) {
 #pragma unroll
                 for (int i = 0; i < 4; i++)
-                    sa[i][w] = *reinterpret_cast<const uint32_t *>(&stS(S, w)[(wm * 128 + i * 32 + l32) * 4]) >> (8 * h);
+                    sa[i][w] = *reinterpret_cast<const uint32_t *>(&tSA[(wm * 128 + i * 32 + l32) * 16 + 4 * w]) >> (8 * h);
 #pragma unroll
                 for (int j = 0; j < 2; j++)
-                    sbw[j][w] = *reinterpret_cast<const uint32_t *>(&stS(S, NSW + w)[(wn * 64 + j * 32 + l32) * 4]) >> (8 * h);
+                    sbw[j][w] = *reinterpret_cast<const uint32_t *>(&tSB[(wn * 64 + j * 32 + l32) * 16 + 4 * w]) >> (8 * h);
             }
+            // Fragments are double-buffered: step s + 1's LDS reads are issued
+            // before step s's MFMAs, and a scheduling fence closes each step,
+            // so at most two steps' fragments are live beside the accumulators.
+            uint4 fa[2][4], fb[2][2];
+            auto load = [&](auto step) {
+                constexpr int s = decltype(step)::value, b = s & 1;
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    fa[b][i] = *reinterpret_cast<const uint4 *>(&tA[swz<RBA>(wm * 128 + i * 32 + l32, 2 * s + h)]);
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    fb[b][j] = *reinterpret_cast<const uint4 *>(&tB[swz<RBB>(wn * 64 + j * 32 + l32, 2 * s + h)]);
+            };
+            load(std::integral_constant<int, 0>{});
             static_for<0, KE / 64>([&](auto step) {
-                constexpr int s = decltype(step)::value;
+                constexpr int s = decltype(step)::value, b = s & 1;
                 constexpr int w = s / 2, sel = (2 * s) % 4;
-                v8i fa[4], fb[2];
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const uint4 t = *reinterpret_cast<const uint4 *>(&tA[swz<RBA>(wm * 128 + i * 32 + l32, 2 * s + h)]);
-                    fa[i] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
-                }
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const uint4 t = *reinterpret_cast<const uint4 *>(&tB[swz<RBB>(wn * 64 + j * 32 + l32, 2 * s + h)]);
-                    fb[j] = v8i{(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
-                }
+                if constexpr (s + 1 < KE / 64) load(std::integral_constant<int, s + 1>{});
 #pragma unroll
                 for (int i = 0; i < 4; i++)
 #pragma unroll
-                    for (int j = 0; j < 2; j++)
+                    for (int j = 0; j < 2; j++) {
+                        const uint4 x = fa[b][i], y = fb[b][j];
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fb[j], fa[i], acc[i][j], 4, 4, sel, (int)sbw[j][w], sel, (int)sa[i][w]);
+                            v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0},
+                            v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0}, acc[i][j], 4, 4, sel,
+                            (int)sbw[j][w], sel, (int)sa[i][w]);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
             });
         } else if constexpr (MODE == 1) {
             float sca[4][4], scb[2][4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int ra_ = wm * 128 + i * 32 + l32;
-                const uint32_t wa = *reinterpret_cast<const uint32_t *>(&stS(S, 0)[ra_ * 4]);
+                const uint32_t wa = *reinterpret_cast<const uint32_t *>(&tSA[ra_ * 16]);
                 const int Ra = sRa[ra_];
 #pragma unroll
                 for (int q = 0; q < 4; q++) sca[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wa >> (8 * q)) & 0xFF) - Ra);
@@ -729,7 +761,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 const int rb_ = wn * 64 + j * 32 + l32;
-                const uint32_t wb = *reinterpret_cast<const uint32_t *>(&stS(S, 1)[rb_ * 4]);
+                const uint32_t wb = *reinterpret_cast<const uint32_t *>(&tSB[rb_ * 16]);
                 const int Rb = sRb[rb_];
 #pragma unroll
                 for (int q = 0; q < 4; q++) scb[j][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wb >> (8 * q)) & 0xFF) - Rb);
@@ -763,7 +795,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                     int sb_r[16];  // scale of column n = 8(r/4) + 4h + r%4 of tile j
 #pragma unroll
                     for (int r = 0; r < 16; r++)
-                        sb_r[r] = stS(S, 1)[(wn * 64 + j * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 4 + blk];
+                        sb_r[r] = tSB[(wn * 64 + j * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 16 + blk];
                     static_for<0, 4>([&](auto ii) {
                         constexpr int i = decltype(ii)::value;
                         v16f p;
@@ -778,7 +810,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                             const v8bf b8 = to_bf16x8<FB>(lo, hi, 1.0f);
                             p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8, a8, p, 0, 0, 0);
                         }
-                        const int sa = stS(S, 0)[(wm * 128 + i * 32 + l32) * 4 + blk];
+                        const int sa = tSA[(wm * 128 + i * 32 + l32) * 16 + blk];
 #pragma unroll
                         for (int r = 0; r < 16; r++) {
                             const float v = __builtin_amdgcn_ldexpf(p[r], sa + sb_r[r] - 254);
@@ -791,20 +823,27 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     };
 
     using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    issue(I0{}, 0);
-    for (int kt0 = 0; kt0 < ntk; kt0 += NS) {
-        // stage u holds tile kt0 + u; after the barrier the other stage's
-        // buffer is free and receives the next tile
-        auto body = [&](auto U, auto NEXT) {
-            const int kt = kt0 + decltype(U)::value;
+    using B1 = std::integral_constant<bool, true>;
+    issue(I0{}, I0{}, B1{}, 0);
+    for (int kt0 = 0; kt0 < ntk; kt0 += 2 * SPS) {
+        // stage kt0 + u sits in code buffer u % 2 and scale slot u / SPS.
+        // After the barrier every wave is done with stage kt0 + u - 1, whose
+        // code buffer receives the next stage (and, at a slot boundary, whose
+        // scale slot receives the next SPS stages' scales).
+        static_for<0, 2 * SPS>([&](auto uu) {
+            constexpr int u = decltype(uu)::value;
+            const int kt = kt0 + u;  // stage computed in this step
             wait_vm<0>();
             barrier();
-            issue(NEXT, kt + 1);
-            if (kt < ntk) compute(U);
-        };
-        body(I0{}, I1{});
-        body(I1{}, I0{});
+            issue(std::integral_constant<int, (u + 1) % 2>{}, std::integral_constant<int, ((u + 1) / SPS) % 2>{},
+                  std::integral_constant<bool, (u + 1) % SPS == 0>{}, kt + 1);
+            // unconditional: a stage past the end holds zero codes and zero
+            // scale bytes (out-of-range loads), which add exactly 0; a branch
+            // here would let the compiler sink the stage's MFMAs past the next
+            // barrier and keep every fragment of the stage live across it
+            compute(std::integral_constant<int, u % 2>{}, std::integral_constant<int, u / SPS>{},
+                    std::integral_constant<int, u % SPS>{});
+        });
     }
     wait_vm<0>();  // drain the out-of-range stage loads before the workgroup ends
 
@@ -910,11 +949,11 @@ template <int FA, int FB>
 hipError_t launch_fmt(const GemmArgs &g, bool bf16, hipStream_t stream) {
     const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(NT);
     constexpr bool fp4 = FA == E2M1 && FB == E2M1;
-    constexpr int KE = fp4 ? 256 : 128;
-    // pipelined kernels: K a whole number of stages, 16-byte aligned codes,
-    // scale rows aligned for the 2- or 4-byte scale loads, offsets in 32 bits
+    // pipelined kernels: K a whole number of scale slots (16 scale bytes =
+    // 512 elements per row), 16-byte aligned codes, dword-aligned scale rows,
+    // offsets in 32 bits
     const int64_t rowA = FA == E2M1 ? g.K / 2 : g.K, rowB = FB == E2M1 ? g.K / 2 : g.K;
-    const bool pipelined = g.K % KE == 0 && ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.b % 16 == 0) &&
+    const bool pipelined = g.K % 512 == 0 && ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.b % 16 == 0) &&
                            ((uintptr_t)g.as % 4 == 0) && ((uintptr_t)g.bs % 4 == 0) &&
                            (int64_t)BM * (rowA > rowB ? rowA : rowB) < ((int64_t)1 << 31);
     if (pipelined) {
