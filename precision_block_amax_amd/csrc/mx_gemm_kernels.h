@@ -77,10 +77,13 @@ __device__ __forceinline__ void static_for(Fn &&f) {
     }
 }
 
-// byte offset of 16-byte chunk `ch` of row `row` in a swizzled LDS tile
+// byte offset of 16-byte chunk `ch` of row `row` in a swizzled LDS tile.
+// 128-byte rows span 32 of the 64 banks, so two consecutive rows fill them;
+// the key (row >> 1) & 7 gives the 16 rows that one pass of a 16-byte-per-lane
+// read touches 16 different 4-bank groups.
 template <int RB>
 __device__ __forceinline__ int swz_key(int row) {
-    if constexpr (RB == 128) return row & 7;
+    if constexpr (RB == 128) return (row >> 1) & 7;
     else if constexpr (RB == 64) return (row >> 1) & 3;  // two rows per 128 bytes
     else return (row >> 2) & 1;                          // 32-byte rows: four rows per 128 bytes
 }
@@ -542,6 +545,22 @@ __device__ __forceinline__ v4i rsrc(const void *base, uint32_t bytes) {
 // would then wait for every load in flight before an LDS read, stays out of
 // it: the kernel waits for the loads explicitly (vmcnt) before its barriers.
 // M0 carries the LDS address and needs one wait state before the load.
+// 4 bytes per lane for the lanes in `mask` only (EXEC is set and restored
+// inside the statement, so no branch splits the caller's code).
+// The mask halves must be wave-uniform; they go through readfirstlane so
+// the compiler keeps them in scalar registers.
+__device__ __forceinline__ void dma4_masked(v4i r, void *lds, int voff, int soff, uint64_t mask) {
+    const uint32_t m = (uint32_t)(uintptr_t)(lds_t)lds;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)mask);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(mask >> 32));
+    uint64_t saved;
+    asm volatile(
+        "s_mov_b64 %0, exec\n\ts_mov_b32 exec_lo, %5\n\ts_mov_b32 exec_hi, %6\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "buffer_load_dword %1, %3, %4 offen lds\n\ts_mov_b64 exec, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(m), "s"(r), "s"(soff), "s"(lo), "s"(hi)
+        : "memory", "m0");
+}
 __device__ __forceinline__ void dma16(v4i r, void *lds, int voff, int soff) {
     const uint32_t m = (uint32_t)(uintptr_t)(lds_t)lds;
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
@@ -609,10 +628,14 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     constexpr int NSW = SBY / 4;                       // scale words per row per stage
     constexpr int SPS = 16 / SBY;                      // stages per scale slot (16 scale bytes per row)
     constexpr int NW = PNT / 64;                       // waves
-    constexpr int NIA = BM * RBA / 1024 / NW, NIB = BN * RBB / 1024 / NW;  // 1 KiB DMA per wave instruction
+    // All eight waves share the stage loads.  (Leaving them to one wave per
+    // SIMD, so that its partner multiplies meanwhile, measured slower on the
+    // gate/up projection GEMM: 629 us against 563 us.)
+    constexpr int NWD = 8;
+    constexpr int NIA = BM * RBA / 1024 / NWD, NIB = BN * RBB / 1024 / NWD;  // 1 KiB DMA per wave instruction
     constexpr int CPRA = RBA / 16, CPRB = RBB / 16;
     static_assert(NIA >= 1 && NIB >= 1, "DMA split");
-    static_assert(NW == 8 && BM == 256 && BN == 256, "one 64-row scale DMA per wave");
+    static_assert(NW == 8 && NWD == NW && BM == 256 && BN == 256, "load split");
 
     // Code stages alternate between two buffers; scale slots (16 bytes per
     // row: the scales of SPS consecutive stages) alternate between two more.
@@ -622,6 +645,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint8_t sB0[BN * RBB], sB1[BN * RBB];
     __shared__ __attribute__((aligned(16))) uint8_t sS0[2][BM * 16], sS1[2][BM * 16];  // [A, B][row * 16 + byte]
     __shared__ int sRa[BM], sRb[BN];
+    __shared__ __attribute__((aligned(16))) uint8_t sPF[256];  // landing area of the L2 prefetches, never read
     auto stA = [&](auto S) -> uint8_t * { if constexpr (decltype(S)::value == 0) return sA0; else return sA1; };
     auto stB = [&](auto S) -> uint8_t * { if constexpr (decltype(S)::value == 0) return sB0; else return sB1; };
     auto stS = [&](auto T, int op) -> uint8_t * { if constexpr (decltype(T)::value == 0) return sS0[op]; else return sS1[op]; };
@@ -662,16 +686,41 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     // per-lane DMA source offsets, constant along K: lane l of instruction q
     // fills LDS bytes [16 l, 16 l + 16) of its 1 KiB segment = physical chunk
     // l % CPR of row seg * (64 / CPR) + l / CPR, i.e. logical chunk pch ^ key.
-    // Instruction q's rows are instruction 0's plus q * 64 / CPR, which leaves
-    // the swizzle key unchanged, so the per-q part is a uniform (scalar) offset.
-    static_assert(64 / CPRA >= 8 && 64 / CPRB >= 8, "row step keeps the swizzle key");
-    const int rowA0 = wave * NIA * (64 / CPRA) + lane / CPRA, rowB0 = wave * NIB * (64 / CPRB) + lane / CPRB;
+    // Instruction q's rows are instruction 0's plus q * 64 / CPR: the row part
+    // is a uniform (scalar) offset, and the swizzle key of 128-byte rows moves
+    // by 8 rows -> key ^ 4, i.e. byte offset ^ 64, on odd q (row strides are
+    // multiples of 128 bytes, so bit 6 belongs to the chunk part); the keys of
+    // 64- and 32-byte rows do not change.
+    static_assert(64 / CPRA == 8 || RBA < 128, "8 rows per instruction");
+    static_assert(64 / CPRB == 8 || RBB < 128, "8 rows per instruction");
+    const int dw = wave;  // index among the loading waves
+    const int rowA0 = dw * NIA * (64 / CPRA) + lane / CPRA, rowB0 = dw * NIB * (64 / CPRB) + lane / CPRB;
     const int voffA = rowA0 * rowA + (((lane % CPRA) ^ swz_key<RBA>(rowA0)) << 4);
     const int voffB = rowB0 * rowB + (((lane % CPRB) ^ swz_key<RBB>(rowB0)) << 4);
+    const int voffA1 = RBA == 128 ? (voffA ^ 64) : voffA, voffB1 = RBB == 128 ? (voffB ^ 64) : voffB;
 
-    // scale slot loads: wave w fetches 16 bytes of each of the 64 rows
-    // 64 (w % 4) .. +63 of operand w / 4 (A, then B); one line per row
-    const int sop = wave >> 2, srow0 = (wave & 3) * 64;
+    // L2 prefetch two stages ahead of the stage loads: every wave issues one
+    // 4-byte-per-lane load per stage (one lane per 128-byte row line), so the
+    // barrier can wait for all but the newest load.  Tiles running side by
+    // side on an XCD (eight tile rows by four tile columns) share rows, so
+    // each touches only its share: a quarter of its A rows, picked by its
+    // column index (first half of the loading waves), and an eighth of its B
+    // rows, picked by its row index (second half).
+    constexpr int PFA = 64 / (NWD / 2), PFB = 32 / (NWD / 2);  // rows per prefetching wave
+    const bool pfB = dw >= NWD / 2;
+    const int pw = dw & (NWD / 2 - 1);
+    const int pf_row0 = pfB ? 32 * ((m0 / BM) & 7) + pw * PFB : 64 * ((n0 / BN) & 3) + pw * PFA;
+    const int pf_voff = (pf_row0 + lane) * (pfB ? rowB : rowA);
+    const uint64_t pf_mask = pfB ? (1ull << PFB) - 1 : (1ull << PFA) - 1;
+    const v4i rPF = pfB ? rB : rA;
+    const int pf_step = pfB ? RBB : RBA;
+    const int pf_nrec = (int)(pfB ? nrecB : nrecA);
+
+    // scale slot loads: eight 64-row instructions (four for A's rows, four
+    // for B's), NSI per loading wave; 16 bytes of each row, one line per row
+    constexpr int NSI = 8 / NWD;
+    const int sop = (dw * NSI) >> 2;
+    const int srow0 = ((dw * NSI) & 3) * 64;
     const int svoff = (srow0 + lane) * kblocks;
 
     // codes of stage kt into code buffer S; with SCALES, also the scales of
@@ -682,15 +731,20 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
         const int soA = live ? kt * RBA : (int)nrecA, soB = live ? kt * RBB : (int)nrecB;
 #pragma unroll
         for (int q = 0; q < NIA; q++)
-            dma16(rA, stA(S) + (wave * NIA + q) * 1024, voffA, soA + q * (64 / CPRA) * rowA);
+            dma16(rA, stA(S) + (dw * NIA + q) * 1024, (q & 1) ? voffA1 : voffA, soA + q * (64 / CPRA) * rowA);
 #pragma unroll
         for (int q = 0; q < NIB; q++)
-            dma16(rB, stB(S) + (wave * NIB + q) * 1024, voffB, soB + q * (64 / CPRB) * rowB);
-        // branch-free (uniform selects): a branch would split the loop body
-        // into blocks, and the compiler would then sink each stage's MFMAs
-        // into the block of their next use, past the barrier
-        if constexpr (decltype(SCALES)::value)
-            dma16(sop ? rSB : rSA, stS(T, sop) + srow0 * 16, svoff, live ? kt * SBY : (int)(sop ? nrecSB : nrecSA));
+            dma16(rB, stB(S) + (dw * NIB + q) * 1024, (q & 1) ? voffB1 : voffB, soB + q * (64 / CPRB) * rowB);
+        // branch-free (uniform selects, EXEC masks): a branch would split the
+        // loop body into blocks, and the compiler would then sink each stage's
+        // MFMAs into the block of their next use, past the barrier
+        if constexpr (decltype(SCALES)::value) {
+#pragma unroll
+            for (int u = 0; u < NSI; u++)
+                dma16(sop ? rSB : rSA, stS(T, sop) + (srow0 + 64 * u) * 16, svoff + 64 * u * kblocks,
+                      live ? kt * SBY : (int)(sop ? nrecSB : nrecSA));
+        }
+        dma4_masked(rPF, sPF, pf_voff, kt + 2 < ntk ? (kt + 2) * pf_step : pf_nrec, pf_mask);
     };
 
     v16f acc[4][2];  // acc[i][j]: C^T tile of A rows i, B rows j
@@ -833,7 +887,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
         static_for<0, 2 * SPS>([&](auto uu) {
             constexpr int u = decltype(uu)::value;
             const int kt = kt0 + u;  // stage computed in this step
-            wait_vm<0>();
+            wait_vm<1>();  // this stage's loads; the newest (the prefetch) may still run
             barrier();
             issue(std::integral_constant<int, (u + 1) % 2>{}, std::integral_constant<int, ((u + 1) / SPS) % 2>{},
                   std::integral_constant<bool, (u + 1) % SPS == 0>{}, kt + 1);
