@@ -39,6 +39,65 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
+// Element casts by the gfx950 scaled conversions (v_cvt_scalef32_pk_*): they
+// convert v / scale, scale = 2^e, rounding to nearest with ties to even and
+// keeping the sign of zero.  E2M1 saturates to +-6, which is exactly the cast
+// of mx_convert.h.  E4M3 and E5M2 would round inputs just below the
+// saturation point up to the NaN / Inf code, so those values are first
+// clamped to +-max_normal * 2^e (one med3), after which the result equals
+// the mx_convert.h cast too.  Both facts were checked on the device against
+// mx_convert.h: every bf16 input at every reachable scale exponent, every
+// fp32 input at e = 0 and strided fp32 sweeps at nine exponents from -127
+// to 125, zero mismatches.  Element 2k goes to the low nibble / byte.
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+template <int F> struct MaxNormal;
+template <> struct MaxNormal<E4M3> { static constexpr float v = 448.0f; };
+template <> struct MaxNormal<E5M2> { static constexpr float v = 57344.0f; };
+
+// four FP8 codes of a..d (fp32) -> bytes 0..3
+template <int F>
+__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d, float s, float lim) {
+    a = __builtin_amdgcn_fmed3f(a, -lim, lim);
+    b = __builtin_amdgcn_fmed3f(b, -lim, lim);
+    c = __builtin_amdgcn_fmed3f(c, -lim, lim);
+    d = __builtin_amdgcn_fmed3f(d, -lim, lim);
+    v2s w = {0, 0};
+    if constexpr (F == E4M3) {
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, s, false);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, s, true);
+    } else {
+        w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, a, b, s, false);
+        w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, c, d, s, true);
+    }
+    return __builtin_bit_cast(uint32_t, w);
+}
+
+// eight E2M1 codes of y[0..7] (fp32) -> nibbles 0..7
+__device__ __forceinline__ uint32_t cvt8_fp4(const float *y, float s) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], s, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], s, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], s, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], s, 3);
+    return w;
+}
+
+// eight E2M1 codes of the bf16 pairs d[0..3] (element 2k in the low half of d[k])
+__device__ __forceinline__ uint32_t cvt8_fp4_bf16(const uint32_t *d, float s) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[0]), s, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[1]), s, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[2]), s, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[3]), s, 3);
+    return w;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
 // Row mode.  Octet o covers elements 8o .. 8o+7 of the row-major [rows x cols]
 // view; cols % 32 == 0 keeps every block inside one quad of lanes.
 template <int F, bool CONTIG, bool VEC>
@@ -82,17 +141,19 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
         m = quad_max(m);  // every lane runs the exchange; out-of-range quads hold zeros
         const bool finite = m < 0x7F80u;
         const int e = scale_exp_bf16<F>(finite ? m : 0u);
-        uint32_t c[8];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            c[2 * i] = finite ? code_from_bf16<F>(w[u][i] & 0xFFFFu, e) : 0u;
-            c[2 * i + 1] = finite ? code_from_bf16<F>(w[u][i] >> 16, e) : 0u;
+        const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
+        uint32_t packed = 0, lo = 0, hi = 0;
+        if constexpr (F == E2M1) {
+            packed = finite ? cvt8_fp4_bf16(w[u], sc) : 0u;
+        } else {
+            const float lim = __builtin_amdgcn_ldexpf(MaxNormal<F>::v, e);
+            lo = cvt4_fp8<F>(bf16_lo(w[u][0]), bf16_hi(w[u][0]), bf16_lo(w[u][1]), bf16_hi(w[u][1]), sc, lim);
+            hi = cvt4_fp8<F>(bf16_lo(w[u][2]), bf16_hi(w[u][2]), bf16_lo(w[u][3]), bf16_hi(w[u][3]), sc, lim);
+            lo = finite ? lo : 0u;
+            hi = finite ? hi : 0u;
         }
         if (o < total_oct) {
             if (F == E2M1) {
-                uint32_t packed = 0;
-#pragma unroll
-                for (int i = 0; i < 8; i++) packed |= c[i] << (4 * i);
                 if (VEC) {
                     *reinterpret_cast<uint32_t *>(codes + (uint64_t)o * 4) = packed;
                 } else {
@@ -100,8 +161,6 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
                     for (int i = 0; i < 4; i++) codes[(uint64_t)o * 4 + i] = (uint8_t)(packed >> (8 * i));
                 }
             } else {
-                const uint32_t lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-                const uint32_t hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
                 if (VEC) {
                     *reinterpret_cast<uint2 *>(codes + (uint64_t)o * 8) = make_uint2(lo, hi);
                 } else {
@@ -146,33 +205,15 @@ __device__ __forceinline__ void hadamard32(float (&y)[32], uint32_t sign_mask) {
     for (int i = 0; i < 32; i++) y[i] = __fmul_rn(y[i], c);
 }
 
-template <int F>
-__device__ __forceinline__ void store_block_codes(uint8_t *dst, const uint32_t (&c)[32], bool vec) {
-    if (F == E2M1) {
-        uint32_t p[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            p[q] = 0;
-#pragma unroll
-            for (int i = 0; i < 8; i++) p[q] |= c[8 * q + i] << (4 * i);
-        }
-        if (vec) {
-            *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; i++) dst[i] = (uint8_t)(p[i >> 2] >> (8 * (i & 3)));
-        }
+// one block's packed code words (4 for E2M1, 8 for FP8) to dst
+template <int NWORD>
+__device__ __forceinline__ void store_block_words(uint8_t *dst, const uint32_t (&p)[NWORD], bool vec) {
+    if (vec) {
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
+        if constexpr (NWORD == 8) *reinterpret_cast<uint4 *>(dst + 16) = make_uint4(p[4], p[5], p[6], p[7]);
     } else {
-        uint32_t p[8];
 #pragma unroll
-        for (int q = 0; q < 8; q++) p[q] = c[4 * q] | (c[4 * q + 1] << 8) | (c[4 * q + 2] << 16) | (c[4 * q + 3] << 24);
-        if (vec) {
-            *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
-            *reinterpret_cast<uint4 *>(dst + 16) = make_uint4(p[4], p[5], p[6], p[7]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; i++) dst[i] = (uint8_t)(p[i >> 2] >> (8 * (i & 3)));
-        }
+        for (int i = 0; i < 4 * NWORD; i++) dst[i] = (uint8_t)(p[i >> 2] >> (8 * (i & 3)));
     }
 }
 
@@ -213,42 +254,32 @@ __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
 #pragma unroll
     for (int j = 0; j < kTrColsPerLane; j++) {
         if (j >= ncols) break;
-        uint32_t c[32];
-        int S;
-        if (ROTATE) {
-            float y[32];
+        float y[32];
 #pragma unroll
-            for (int i = 0; i < 32; i++) {
-                const uint32_t d = w[i][j >> 1];
-                y[i] = __uint_as_float((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
-            }
-            hadamard32(y, sign_mask);
-            uint32_t m = 0;
+        for (int i = 0; i < 32; i++) y[i] = (j & 1) ? bf16_hi(w[i][j >> 1]) : bf16_lo(w[i][j >> 1]);
+        if (ROTATE) hadamard32(y, sign_mask);
+        uint32_t m = 0;
 #pragma unroll
-            for (int i = 0; i < 32; i++) m = umax(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
-            const bool finite = m < 0x7F800000u;
-            const int e = scale_exp_f32<F>(finite ? m : 0u);
+        for (int i = 0; i < 32; i++) m = umax(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+        // bf16 inputs are exact in fp32, so the fp32 scale rule gives the bf16 one
+        const bool finite = m < 0x7F800000u;
+        const int e = scale_exp_f32<F>(finite ? m : 0u);
+        const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
+        constexpr int NWORD = F == E2M1 ? 4 : 8;
+        uint32_t p[NWORD];
+        if constexpr (F == E2M1) {
 #pragma unroll
-            for (int i = 0; i < 32; i++) c[i] = finite ? code_from_f32<F>(y[i], e) : 0u;
-            S = finite ? e + 127 : 0xFF;
+            for (int q = 0; q < 4; q++) p[q] = cvt8_fp4(y + 8 * q, sc);
         } else {
-            uint32_t b[32];
-            uint32_t m = 0;
+            const float lim = __builtin_amdgcn_ldexpf(MaxNormal<F>::v, e);
 #pragma unroll
-            for (int i = 0; i < 32; i++) {
-                const uint32_t d = w[i][j >> 1];
-                b[i] = (j & 1) ? (d >> 16) : (d & 0xFFFFu);
-                m = umax(m, b[i] & 0x7FFFu);
-            }
-            const bool finite = m < 0x7F80u;
-            const int e = scale_exp_bf16<F>(finite ? m : 0u);
-#pragma unroll
-            for (int i = 0; i < 32; i++) c[i] = finite ? code_from_bf16<F>(b[i], e) : 0u;
-            S = finite ? e + 127 : 0xFF;
+            for (int q = 0; q < 8; q++) p[q] = cvt4_fp8<F>(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3], sc, lim);
         }
+#pragma unroll
+        for (int q = 0; q < NWORD; q++) p[q] = finite ? p[q] : 0u;
         const int64_t col = c0 + j;
-        store_block_codes<F>(codes + col * row_bytes + rb * (F == E2M1 ? 16 : 32), c, VEC);
-        scales[col * nrb + rb] = (uint8_t)S;
+        store_block_words<NWORD>(codes + col * row_bytes + rb * (F == E2M1 ? 16 : 32), p, VEC);
+        scales[col * nrb + rb] = (uint8_t)(finite ? e + 127 : 0xFF);
     }
 }
 
