@@ -18,9 +18,11 @@
 //              8-byte loads, each wave instruction reading 512 contiguous
 //              bytes of one row), so a whole block sits in one lane's
 //              registers: amax and, for the rotation, the five butterfly
-//              stages need no cross-lane traffic and no LDS.  The four waves
-//              of a workgroup take four consecutive row blocks, so each output
-//              row receives 128 contiguous code bytes (FP8) from one workgroup.
+//              stages need no cross-lane traffic.  A workgroup covers 8 row
+//              blocks; its codes are staged in LDS and stored as whole
+//              128-byte (E2M1) or 256-byte (FP8) runs of each output row, since
+//              one 16-byte store per lane and output row wrote at about a
+//              third of the read rate.
 #include "mx_internal.h"
 
 namespace mx {
@@ -178,10 +180,17 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
 
 // ---------------------------------------------------------------------------
 // Transposed mode, optionally after the rotation.  Lane: 4 columns
-// c0 .. c0+3; wave: row block rb (32 rows); workgroup: 4 row blocks x 256
-// columns.
+// c0 .. c0+3 of one 32-row block at a time (one 8-byte load per row, each
+// wave instruction reading 512 contiguous bytes of a row), so the block's
+// amax and the rotation's butterflies stay in the lane's registers.  A
+// workgroup covers 256 columns x 8 row blocks, one block per wave.  The codes
+// are staged in LDS and written out afterwards as whole
+// 128-byte (E2M1) or 256-byte (FP8) runs of each output row, and the 8 scale
+// bytes of each output row as one 8-byte store.
 constexpr int kTrColsPerLane = 4;
-constexpr int kTrWaves = 4;
+constexpr int kTrWaves = 8;
+constexpr int kTrBlocks = 8;   // row blocks per workgroup
+constexpr int kTrCols = 256;   // columns per workgroup
 
 // y = c * H32 * diag(s) * x, stages h = 1, 2, 4, 8, 16, one fp32 rounding per op
 __device__ __forceinline__ void hadamard32(float (&y)[32], uint32_t sign_mask) {
@@ -205,81 +214,117 @@ __device__ __forceinline__ void hadamard32(float (&y)[32], uint32_t sign_mask) {
     for (int i = 0; i < 32; i++) y[i] = __fmul_rn(y[i], c);
 }
 
-// one block's packed code words (4 for E2M1, 8 for FP8) to dst
-template <int NWORD>
-__device__ __forceinline__ void store_block_words(uint8_t *dst, const uint32_t (&p)[NWORD], bool vec) {
-    if (vec) {
-        *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
-        if constexpr (NWORD == 8) *reinterpret_cast<uint4 *>(dst + 16) = make_uint4(p[4], p[5], p[6], p[7]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4 * NWORD; i++) dst[i] = (uint8_t)(p[i >> 2] >> (8 * (i & 3)));
-    }
-}
-
 template <int F, bool ROTATE, bool VEC>
 __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
     const uint16_t *__restrict__ x, int64_t ldx, int64_t rows, int64_t cols, uint32_t sign_mask,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    constexpr int BB = F == E2M1 ? 16 : 32;             // code bytes per block of one output row
+    constexpr int CB = kTrBlocks * BB;                  // staged bytes per output row: 128 or 256
+    constexpr int NCH = CB / 16;                        // 16-byte chunks per output row
+    __shared__ __attribute__((aligned(16))) uint8_t sC[kTrCols * CB];
+    __shared__ __attribute__((aligned(8))) uint8_t sS[kTrCols * kTrBlocks];
+    // chunk q of output row c sits at c * CB + ((q ^ key(c)) << 4): the 16
+    // lanes of one LDS write pass hold columns 4L + j, whose keys differ
+    const auto key = [](int c) { return (c >> 2) & (NCH - 1); };
+
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * kTrColsPerLane;
-    const int64_t rb = (int64_t)blockIdx.y * kTrWaves + wave;
+    const int64_t ctile = (int64_t)blockIdx.x * kTrCols;
+    const int64_t rb0 = (int64_t)blockIdx.y * kTrBlocks;
     const int64_t nrb = rows / 32;
-    if (rb >= nrb || c0 >= cols) return;  // no barriers or cross-lane ops below
-    const int ncols = (int)((cols - c0) < kTrColsPerLane ? (cols - c0) : kTrColsPerLane);
+    const int nb = (int)((nrb - rb0) < kTrBlocks ? (nrb - rb0) : kTrBlocks);    // valid blocks
+    const int nc = (int)((cols - ctile) < kTrCols ? (cols - ctile) : kTrCols);  // valid columns
+    const int cl = lane * kTrColsPerLane;                                        // lane's first column in the tile
+    const int ncols = nc - cl < kTrColsPerLane ? (nc - cl < 0 ? 0 : nc - cl) : kTrColsPerLane;
 
-    // w[i][0] = columns c0, c0+1 of row 32 rb + i; w[i][1] = columns c0+2, c0+3
-    uint32_t w[32][2];
-    const uint16_t *p = x + rb * 32 * ldx + c0;
-    if (VEC && ncols == kTrColsPerLane) {
+    static_assert(kTrWaves == kTrBlocks, "one block per wave");
+    const int b = wave;  // block within the workgroup
+    if (b < nb && ncols > 0) {  // the barrier below is reached by every wave
+        const int64_t rb = rb0 + b;
+        // w[i][0] = columns c0, c0+1 of row 32 rb + i; w[i][1] = columns c0+2, c0+3
+        uint32_t w[32][2];
+        const uint16_t *p = x + rb * 32 * ldx + ctile + cl;
+        if (VEC && ncols == kTrColsPerLane) {
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
-            const uint2 t = *reinterpret_cast<const uint2 *>(p + i * ldx);
-            w[i][0] = t.x;
-            w[i][1] = t.y;
+            for (int i = 0; i < 32; i++) {
+                const uint2 t = *reinterpret_cast<const uint2 *>(p + i * ldx);
+                w[i][0] = t.x;
+                w[i][1] = t.y;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                uint32_t v[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) v[j] = j < ncols ? p[i * ldx + j] : 0u;
+                w[i][0] = v[0] | (v[1] << 16);
+                w[i][1] = v[2] | (v[3] << 16);
+            }
         }
-    } else {
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
-            uint32_t v[4];
+        for (int j = 0; j < kTrColsPerLane; j++) {
+            if (j >= ncols) break;
+            float y[32];
 #pragma unroll
-            for (int j = 0; j < 4; j++) v[j] = j < ncols ? p[i * ldx + j] : 0u;
-            w[i][0] = v[0] | (v[1] << 16);
-            w[i][1] = v[2] | (v[3] << 16);
+            for (int i = 0; i < 32; i++) y[i] = (j & 1) ? bf16_hi(w[i][j >> 1]) : bf16_lo(w[i][j >> 1]);
+            if (ROTATE) hadamard32(y, sign_mask);
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 32; i++) m = umax(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+            // bf16 inputs are exact in fp32, so the fp32 scale rule gives the bf16 one
+            const bool finite = m < 0x7F800000u;
+            const int e = scale_exp_f32<F>(finite ? m : 0u);
+            const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
+            const int c = cl + j;
+            if constexpr (F == E2M1) {
+                uint32_t q[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) q[k] = finite ? cvt8_fp4(y + 8 * k, sc) : 0u;
+                *reinterpret_cast<uint4 *>(&sC[c * CB + ((b ^ key(c)) << 4)]) = make_uint4(q[0], q[1], q[2], q[3]);
+            } else {
+                const float lim = __builtin_amdgcn_ldexpf(MaxNormal<F>::v, e);
+                uint32_t q[8];
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    const uint32_t v = cvt4_fp8<F>(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3], sc, lim);
+                    q[k] = finite ? v : 0u;
+                }
+                *reinterpret_cast<uint4 *>(&sC[c * CB + (((2 * b) ^ key(c)) << 4)]) = make_uint4(q[0], q[1], q[2], q[3]);
+                *reinterpret_cast<uint4 *>(&sC[c * CB + (((2 * b + 1) ^ key(c)) << 4)]) = make_uint4(q[4], q[5], q[6], q[7]);
+            }
+            sS[c * kTrBlocks + b] = (uint8_t)(finite ? e + 127 : 0xFF);
         }
     }
+    __syncthreads();
 
+    // write-out: thread t copies chunk t % NCH of output row t / NCH (+ 256 / NCH per step)
     const int64_t row_bytes = (F == E2M1) ? rows / 2 : rows;
+    const int vchunks = nb * BB / 16;                   // valid chunks per output row
 #pragma unroll
-    for (int j = 0; j < kTrColsPerLane; j++) {
-        if (j >= ncols) break;
-        float y[32];
-#pragma unroll
-        for (int i = 0; i < 32; i++) y[i] = (j & 1) ? bf16_hi(w[i][j >> 1]) : bf16_lo(w[i][j >> 1]);
-        if (ROTATE) hadamard32(y, sign_mask);
-        uint32_t m = 0;
-#pragma unroll
-        for (int i = 0; i < 32; i++) m = umax(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
-        // bf16 inputs are exact in fp32, so the fp32 scale rule gives the bf16 one
-        const bool finite = m < 0x7F800000u;
-        const int e = scale_exp_f32<F>(finite ? m : 0u);
-        const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
-        constexpr int NWORD = F == E2M1 ? 4 : 8;
-        uint32_t p[NWORD];
-        if constexpr (F == E2M1) {
-#pragma unroll
-            for (int q = 0; q < 4; q++) p[q] = cvt8_fp4(y + 8 * q, sc);
+    for (int k = 0; k < kTrCols * NCH / (64 * kTrWaves); k++) {
+        const int t = k * 64 * kTrWaves + threadIdx.x;
+        const int c = t / NCH, q = t % NCH;
+        if (c >= nc || q >= vchunks) continue;
+        const uint4 v = *reinterpret_cast<const uint4 *>(&sC[c * CB + ((q ^ key(c)) << 4)]);
+        uint8_t *dst = codes + (ctile + c) * row_bytes + rb0 * BB + q * 16;
+        if (VEC) {
+            *reinterpret_cast<uint4 *>(dst) = v;
         } else {
-            const float lim = __builtin_amdgcn_ldexpf(MaxNormal<F>::v, e);
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int q = 0; q < 8; q++) p[q] = cvt4_fp8<F>(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3], sc, lim);
+            for (int i = 0; i < 16; i++) dst[i] = (uint8_t)(vv[i >> 2] >> (8 * (i & 3)));
         }
-#pragma unroll
-        for (int q = 0; q < NWORD; q++) p[q] = finite ? p[q] : 0u;
-        const int64_t col = c0 + j;
-        store_block_words<NWORD>(codes + col * row_bytes + rb * (F == E2M1 ? 16 : 32), p, VEC);
-        scales[col * nrb + rb] = (uint8_t)(finite ? e + 127 : 0xFF);
+    }
+    {
+        const int c = threadIdx.x;  // one output row's 8 scale bytes per thread
+        if (c < nc) {
+            uint8_t *dst = scales + (ctile + c) * nrb + rb0;
+            if (nb == kTrBlocks && (((uintptr_t)dst & 7) == 0)) {
+                *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(&sS[c * kTrBlocks]);
+            } else {
+                for (int i = 0; i < nb; i++) dst[i] = sS[c * kTrBlocks + i];
+            }
+        }
     }
 }
 
@@ -310,8 +355,7 @@ template <int F, bool ROTATE>
 hipError_t launch_tr_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint32_t mask,
                          uint8_t *codes, uint8_t *scales, hipStream_t stream) {
     const bool vec = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0) && ((uintptr_t)codes % 16 == 0);
-    const dim3 grid((unsigned)((cols + 64 * kTrColsPerLane - 1) / (64 * kTrColsPerLane)),
-                    (unsigned)((rows / 32 + kTrWaves - 1) / kTrWaves));
+    const dim3 grid((unsigned)((cols + kTrCols - 1) / kTrCols), (unsigned)((rows / 32 + kTrBlocks - 1) / kTrBlocks));
     if (vec)
         hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true>), grid, dim3(64 * kTrWaves), 0, stream, x, ldx,
                            rows, cols, mask, codes, scales);
