@@ -15,7 +15,8 @@ The pages quote their gains on Llama-3.1-8B pre-training on MI355X
 (FP4-training article on hzrcw.cc, section 03); these are that model's
 linear-layer shapes.  `value` is the step's GEMM work divided by the whole
 step time (quantizers included), in TFLOP/s.  Each kernel is also timed with
-HIP events on the stream it runs on and reported against its roofline.
+HIP events on the stream it runs on and reported against its roofline, both
+inside the step and alone after a clean fill of the last-level cache.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -307,6 +308,27 @@ def main() -> int:
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     print("bench: timed %d steps, %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
 
+    # Each kernel again on its own: the last-level cache (256 MB) is first
+    # filled with clean lines by reading a 512 MiB buffer, so the kernel
+    # neither finds its inputs cached nor pays for writing back dirty lines
+    # left by the previous kernel (inside the step a quantizer that follows a
+    # GEMM does, which can halve its read rate).  Median of five.
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1, dtype=torch.int64, device="cuda")
+    isolated = []
+    for (_, _, _, fn) in step.launches:
+        ts = []
+        for _ in range(5):
+            sink.copy_(flush.view(torch.int64).sum().view(1))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        isolated.append(float(np.median(ts)))
+    del flush
+
     if args.calibrate_copy:
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -317,15 +339,18 @@ def main() -> int:
     kernels = []
     for i, (name, kind, work, _) in enumerate(step.launches):
         ms = float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
+        iso = isolated[i]
         if kind == "quant":
-            ach = work / (ms * 1e-3) / 1e9
+            ach, iach = work / (ms * 1e-3) / 1e9, work / (iso * 1e-3) / 1e9
             kernels.append({"kernel": name, "ms": ms, "bound": "hbm", "achieved": ach, "unit": "GB/s",
-                            "peak": PEAK_HBM_GBPS, "frac": ach / PEAK_HBM_GBPS, "work": work})
+                            "peak": PEAK_HBM_GBPS, "frac": ach / PEAK_HBM_GBPS, "work": work,
+                            "isolated": {"ms": iso, "achieved": iach, "frac": iach / PEAK_HBM_GBPS}})
         else:
             arith = kind.split(":")[1]
-            ach = work / (ms * 1e-3) / 1e12
+            ach, iach = work / (ms * 1e-3) / 1e12, work / (iso * 1e-3) / 1e12
             k = {"kernel": name, "ms": ms, "bound": "mfma", "achieved": ach, "unit": "TFLOP/s",
-                 "peak": PEAK_TFLOPS[arith], "frac": ach / PEAK_TFLOPS[arith], "arith": arith, "work": work}
+                 "peak": PEAK_TFLOPS[arith], "frac": ach / PEAK_TFLOPS[arith], "arith": arith, "work": work,
+                 "isolated": {"ms": iso, "achieved": iach, "frac": iach / PEAK_TFLOPS[arith]}}
             if arith == "bf16":  # MXFP8 operands carried as bf16: also against the MXFP8 peak
                 k["frac_of_mxfp8_peak"] = ach / PEAK_TFLOPS["fp8"]
             kernels.append(k)
@@ -336,6 +361,7 @@ def main() -> int:
                 "unit": dom["unit"], "frac": round(dom["frac"], 4), "traffic": traffic, "kernel": dom["kernel"]}
     q = [k for k in kernels if k["bound"] == "hbm"]
     quant_gbps = sum(k["work"] for k in q) / (sum(k["ms"] for k in q) * 1e-3) / 1e9
+    quant_gbps_iso = sum(k["work"] for k in q) / (sum(k["isolated"]["ms"] for k in q) * 1e-3) / 1e9
 
     value = step.flops / (ms_per_step * 1e-3) / 1e12
     line = {
@@ -347,16 +373,21 @@ def main() -> int:
                    "gemms": [k["kernel"] for k in kernels if k["bound"] == "mfma"]},
         "roofline": roofline,
         "quantize_GBps": round(quant_gbps, 1), "quantize_frac_of_hbm_peak": round(quant_gbps / PEAK_HBM_GBPS, 4),
-        "kernels": [{kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in k.items() if kk != "work"}
-                    for k in kernels],
+        "quantize_GBps_isolated": round(quant_gbps_iso, 1),
+        "quantize_frac_of_hbm_peak_isolated": round(quant_gbps_iso / PEAK_HBM_GBPS, 4),
+        "kernels": [{kk: (round(v, 4) if isinstance(v, float) else
+                          {a: round(b, 4) for a, b in v.items()} if isinstance(v, dict) else v)
+                     for kk, v in k.items() if kk != "work"} for k in kernels],
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle on a bounded sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.seed, step.flops)
     if args.kernels:
+        print("%-70s %21s %7s   %s" % ("kernel", "in the step", "", "alone, clean cache"), file=sys.stderr)
         for k in kernels:
-            print("%-70s %8.1f us  %9.1f %s  %5.1f%%" % (k["kernel"], k["ms"] * 1e3, k["achieved"], k["unit"],
-                                                       100 * k["frac"]), file=sys.stderr)
+            print("%-70s %8.1f us %9.1f %s %5.1f%%   %8.1f us %5.1f%%" % (
+                k["kernel"], k["ms"] * 1e3, k["achieved"], k["unit"], 100 * k["frac"],
+                k["isolated"]["ms"] * 1e3, 100 * k["isolated"]["frac"]), file=sys.stderr)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -238,3 +238,51 @@ def test_bad_arguments_raise(mx):
         mx.quantize(x, "e4m3")                  # cols % 32 != 0
     with pytest.raises(mx.MXError):
         mx.quantize_transpose(x[:40], "e4m3")   # rows % 32 != 0
+
+
+EMAX = {"e4m3": 8, "e5m2": 15, "e2m1": 2}
+
+
+def exhaustive_blocks(fmt):
+    """Every finite bf16 value at every reachable block scale exponent e.
+
+    For each e, blocks lead with the largest bf16 of the binade [2^(e+emax),
+    2^(e+emax+1)) (alternating sign), which fixes the block's scale at e; the
+    other 31 elements run through every finite bf16 pattern of either sign
+    whose magnitude does not exceed it (zeros pad the last block).  Returns a
+    [rows x 4096] bf16 bit matrix of whole blocks."""
+    em = EMAX[fmt]
+    mags = np.arange(0x7F80, dtype=np.uint32)
+    parts = []
+    for e in range(-127, 128):
+        k = e + em                                   # floor(log2 amax)
+        if k > 127 or k < -133:
+            continue
+        top = ((k + 127) << 7) | 0x7F if k >= -126 else (1 << (k + 134)) - 1
+        p = mags[mags <= top]
+        vals = np.concatenate([p, p | 0x8000]).astype(np.uint16)
+        n = -(-vals.size // 31)
+        body = np.zeros(n * 31, np.uint16)
+        body[:vals.size] = vals
+        head = np.full((n, 1), top, np.uint16)
+        head[1::2] |= 0x8000
+        parts.append(np.concatenate([head, body.reshape(n, 31)], axis=1))
+    b = np.concatenate(parts)
+    nb = -(-b.shape[0] // 128) * 128
+    out = np.zeros((nb, 32), np.uint16)
+    out[:b.shape[0]] = b
+    return out.reshape(nb // 128, 4096)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_every_bf16_at_every_scale(mx, fmt):
+    """The element casts (the gfx950 scaled conversion instructions, bf16 form
+    in row mode and fp32 form in transposed mode) equal the oracle on every
+    finite bf16 input at every reachable scale exponent."""
+    x = exhaustive_blocks(fmt)
+    want = oracle.quantize(x, fmt)
+    _cmp(mx.quantize(to_dev_bf16(x), fmt), want, "row, every bf16 x every e")
+    xt = np.ascontiguousarray(x.T)                   # the same blocks, now along rows
+    _cmp(mx.quantize_transpose(to_dev_bf16(xt), fmt), oracle.quantize_transpose(xt, fmt),
+         "transposed, every bf16 x every e")
+    assert np.array_equal(oracle.quantize_transpose(xt, fmt)[0], want[0])
