@@ -327,6 +327,37 @@ def main() -> int:
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         isolated.append(float(np.median(ts)))
+
+    def alone(fn):
+        ts = []
+        for _ in range(5):
+            sink.copy_(flush.view(torch.int64).sum().view(1))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    # The fused dual-direction quantizer (one read, row form + rotated
+    # transposed form) on the down-projection output gradient, against the
+    # two single-direction calls it replaces; each alone, clean cache.
+    cfg3 = workloads.config(3)
+    dy = torch.from_numpy(workloads.draw_tensor(cfg3, "dY", seed=args.seed).view(np.int16)).view(
+        torch.bfloat16).to("cuda")
+    outs = mx.quantize_dual(dy, "e2m1", "e2m1", True, 0)
+    r_out, t_out = outs[:2], outs[2:]
+    t_dual = alone(lambda: mx.quantize_dual(dy, "e2m1", "e2m1", True, 0, out=outs))
+    t_row = alone(lambda: mx.quantize(dy, "e2m1", out=r_out))
+    t_rot = alone(lambda: mx.hadamard32_quantize(dy, "e2m1", 0, out=t_out))
+    n_el = dy.numel()
+    dual_bytes = n_el * (2.0 + 2 * (0.5 + 1.0 / 32))
+    fused_dual = {"tensor": "%s/dY %dx%d" % (cfg3.name, dy.shape[0], dy.shape[1]), "formats": "e2m1 row + e2m1 rotated",
+                  "ms": round(t_dual, 4), "GBps": round(dual_bytes / (t_dual * 1e-3) / 1e9, 1),
+                  "frac_of_hbm_peak": round(dual_bytes / (t_dual * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                  "separate_ms": round(t_row + t_rot, 4), "speedup": round((t_row + t_rot) / t_dual, 3)}
+    del dy, outs, r_out, t_out
     del flush
 
     if args.calibrate_copy:
@@ -374,6 +405,7 @@ def main() -> int:
         "roofline": roofline,
         "quantize_GBps": round(quant_gbps, 1), "quantize_frac_of_hbm_peak": round(quant_gbps / PEAK_HBM_GBPS, 4),
         "quantize_GBps_isolated": round(quant_gbps_iso, 1),
+        "fused_dual": fused_dual,
         "quantize_frac_of_hbm_peak_isolated": round(quant_gbps_iso / PEAK_HBM_GBPS, 4),
         "kernels": [{kk: (round(v, 4) if isinstance(v, float) else
                           {a: round(b, 4) for a, b in v.items()} if isinstance(v, dict) else v)
@@ -388,6 +420,9 @@ def main() -> int:
             print("%-70s %8.1f us %9.1f %s %5.1f%%   %8.1f us %5.1f%%" % (
                 k["kernel"], k["ms"] * 1e3, k["achieved"], k["unit"], 100 * k["frac"],
                 k["isolated"]["ms"] * 1e3, 100 * k["isolated"]["frac"]), file=sys.stderr)
+        print("fused dual quantize (%s, %s): %.1f us alone, %.1f%% of HBM; the two single calls: %.1f us" % (
+            fused_dual["tensor"], fused_dual["formats"], fused_dual["ms"] * 1e3, 100 * fused_dual["frac_of_hbm_peak"],
+            fused_dual["separate_ms"] * 1e3), file=sys.stderr)
     print(json.dumps(line), flush=True)
     return 0
 

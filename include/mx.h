@@ -130,6 +130,24 @@ mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t col
                                    void *stream);
 
 /*
+ * mx_quantize_dual -- the row form and the transposed form of x from one
+ * read of x: codes_row / scales_row exactly as mx_quantize(x, fmt_row), and
+ * codes_t / scales_t exactly as mx_quantize_transpose(x, fmt_t) (rotate = 0)
+ * or mx_hadamard32_quantize(x, sign_mask, fmt_t) (rotate = 1).
+ *   rows, cols  both multiples of 32
+ *   rotate      0 or 1
+ * A linear layer needs both forms of its activations, output gradients and
+ * weights: the row form for Fprop and Dgrad, the transposed (for the
+ * gradients, rotated) form for Dgrad's weight and for the weight gradient
+ * (FP4-training article on hzrcw.cc, section 02).  The four output buffers
+ * must not overlap each other or x.
+ */
+mx_status_t mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                             mx_format_t fmt_row, void *codes_row, void *scales_row,
+                             mx_format_t fmt_t, int rotate, uint32_t sign_mask, void *codes_t,
+                             void *scales_t, void *stream);
+
+/*
  * mx_gemm -- C[m, n] = sum_k A[m, k] * B[n, k] over two MX operands, both
  * with the reduction dimension K contiguous ("TN"):
  *   a_codes [M x K] (FP8) or [M x K/2] (E2M1), a_scales [M x K/32]
@@ -137,8 +155,11 @@ mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t col
  *   A[m, k] = decode(code) * 2^(S - 127), same for B
  *   K       multiple of 32
  *   c       [M x ldc] fp32 or bf16 (per `out`), ldc >= N
- * Products are formed by the gfx950 block-scaled matrix instructions and
- * accumulated in fp32 in steps of 64 along K.  Fprop: A = X, B = W.
+ * E2M1 x E2M1 products are formed by the gfx950 block-scaled matrix
+ * instruction (64 elements of K per step, exact), pairs with an FP8 operand
+ * by the bf16 matrix instruction on codes converted exactly to bf16 against
+ * a per-row reference scale; partial sums are accumulated in fp32, so
+ * |C - sum| <= 1e-5 * sum |A[m, k] * B[n, k]|.  Fprop: A = X, B = W.
  * Dgrad: A = dY, B = W^T (from mx_quantize_transpose).  Wgrad: A = dY^T,
  * B = X^T (both from mx_hadamard32_quantize or mx_quantize_transpose).
  * Any pair of formats is accepted.

@@ -110,6 +110,25 @@ mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t col
                                                   (hipStream_t)stream));
 }
 
+mx_status_t mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt_row,
+                             void *codes_row, void *scales_row, mx_format_t fmt_t, int rotate, uint32_t sign_mask,
+                             void *codes_t, void *scales_t, void *stream) {
+    if (rotate != 0 && rotate != 1) return MX_ERR_INVALID_ARG;
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt_row, codes_row, scales_row, false);
+    if (st != MX_OK) return st;
+    if ((st = check_quant(x_bf16, rows, cols, ldx, fmt_t, codes_t, scales_t, true)) != MX_OK) return st;
+    if (rows == 0 || cols == 0) return MX_OK;
+    const int64_t n = rows * cols;
+    const int64_t crb = code_bytes(n, fmt_row), ctb = code_bytes(n, fmt_t), sb = n / 32;
+    if (overlap(codes_row, crb, codes_t, ctb) || overlap(codes_row, crb, scales_t, sb) ||
+        overlap(scales_row, sb, codes_t, ctb) || overlap(scales_row, sb, scales_t, sb))
+        return MX_ERR_INVALID_ARG;
+    if ((st = check_device()) != MX_OK) return st;
+    return launched(mx::launch_quantize_dual((const uint16_t *)x_bf16, rows, cols, ldx, fmt_row, (uint8_t *)codes_row,
+                                             (uint8_t *)scales_row, fmt_t, rotate != 0, sign_mask, (uint8_t *)codes_t,
+                                             (uint8_t *)scales_t, (hipStream_t)stream));
+}
+
 mx_status_t mx_gemm(const void *a_codes, const void *a_scales, mx_format_t fa, const void *b_codes,
                     const void *b_scales, mx_format_t fb, int64_t M, int64_t N, int64_t K, void *c,
                     mx_out_t out, int64_t ldc, void *stream) {

@@ -39,6 +39,11 @@ hipError_t launch_quantize_transpose(const uint16_t *x, int64_t rows, int64_t co
                                      int fmt, bool rotate, uint32_t sign_mask, uint8_t *codes,
                                      uint8_t *scales, hipStream_t stream);
 
+// one read of x: row form (fmt_r) and transposed form (fmt_t, rotated or not)
+hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt_r,
+                                uint8_t *codes_r, uint8_t *scales_r, int fmt_t, bool rotate, uint32_t sign_mask,
+                                uint8_t *codes_t, uint8_t *scales_t, hipStream_t stream);
+
 // GEMM launcher (mx_gemm.hip).
 hipError_t launch_gemm(const uint8_t *a, const uint8_t *as, int fa, const uint8_t *b,
                        const uint8_t *bs, int fb, int64_t M, int64_t N, int64_t K, void *c,

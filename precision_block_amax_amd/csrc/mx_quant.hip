@@ -23,310 +23,10 @@
 //              128-byte (E2M1) or 256-byte (FP8) runs of each output row, since
 //              one 16-byte store per lane and output row wrote at about a
 //              third of the read rate.
-#include "mx_internal.h"
+#include "mx_quant_kernels.h"
 
 namespace mx {
 namespace {
-
-constexpr uint32_t kRowThreads = 256;
-constexpr uint32_t kRowUnroll = 4;  // 16-byte loads in flight per lane
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-// max over the four lanes of a DPP quad (lanes 4q .. 4q+3)
-__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
-    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));  // lane ^ 1
-    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));  // lane ^ 2
-    return v;
-}
-
-// ---------------------------------------------------------------------------
-// Element casts by the gfx950 scaled conversions (v_cvt_scalef32_pk_*): they
-// convert v / scale, scale = 2^e, rounding to nearest with ties to even and
-// keeping the sign of zero.  E2M1 saturates to +-6, which is exactly the cast
-// of mx_convert.h.  E4M3 and E5M2 would round inputs just below the
-// saturation point up to the NaN / Inf code, so those values are first
-// clamped to +-max_normal * 2^e (one med3), after which the result equals
-// the mx_convert.h cast too.  Both facts were checked on the device against
-// mx_convert.h: every bf16 input at every reachable scale exponent, every
-// fp32 input at e = 0 and strided fp32 sweeps at nine exponents from -127
-// to 125, zero mismatches.  Element 2k goes to the low nibble / byte.
-typedef short v2s __attribute__((ext_vector_type(2)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-template <int F> struct MaxNormal;
-template <> struct MaxNormal<E4M3> { static constexpr float v = 448.0f; };
-template <> struct MaxNormal<E5M2> { static constexpr float v = 57344.0f; };
-
-// four FP8 codes of a..d (fp32) -> bytes 0..3
-template <int F>
-__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d, float s, float lim) {
-    a = __builtin_amdgcn_fmed3f(a, -lim, lim);
-    b = __builtin_amdgcn_fmed3f(b, -lim, lim);
-    c = __builtin_amdgcn_fmed3f(c, -lim, lim);
-    d = __builtin_amdgcn_fmed3f(d, -lim, lim);
-    v2s w = {0, 0};
-    if constexpr (F == E4M3) {
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, s, false);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, s, true);
-    } else {
-        w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, a, b, s, false);
-        w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, c, d, s, true);
-    }
-    return __builtin_bit_cast(uint32_t, w);
-}
-
-// eight E2M1 codes of y[0..7] (fp32) -> nibbles 0..7
-__device__ __forceinline__ uint32_t cvt8_fp4(const float *y, float s) {
-    uint32_t w = 0;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], s, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], s, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], s, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], s, 3);
-    return w;
-}
-
-// eight E2M1 codes of the bf16 pairs d[0..3] (element 2k in the low half of d[k])
-__device__ __forceinline__ uint32_t cvt8_fp4_bf16(const uint32_t *d, float s) {
-    uint32_t w = 0;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[0]), s, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[1]), s, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[2]), s, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[3]), s, 3);
-    return w;
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
-
-// ---------------------------------------------------------------------------
-// Row mode.  Octet o covers elements 8o .. 8o+7 of the row-major [rows x cols]
-// view; cols % 32 == 0 keeps every block inside one quad of lanes.
-template <int F, bool CONTIG, bool VEC>
-__global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
-    const uint16_t *__restrict__ x, int64_t ldx, uint32_t total_oct, uint32_t oct_per_row,
-    FastDiv row_div, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
-    const uint32_t o0 = blockIdx.x * (kRowThreads * kRowUnroll) + threadIdx.x;
-    uint32_t w[kRowUnroll][4];
-
-#pragma unroll
-    for (uint32_t u = 0; u < kRowUnroll; u++) {
-        const uint32_t o = o0 + u * kRowThreads;
-        w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0;
-        if (o < total_oct) {
-            const uint16_t *p;
-            if (CONTIG) {
-                p = x + (uint64_t)o * 8;
-            } else {
-                const uint32_t r = row_div.div(o);
-                p = x + (int64_t)r * ldx + (uint64_t)(o - r * oct_per_row) * 8;
-            }
-            if (VEC) {
-                const uint4 t = *reinterpret_cast<const uint4 *>(p);
-                w[u][0] = t.x; w[u][1] = t.y; w[u][2] = t.z; w[u][3] = t.w;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; i++) w[u][i] = (uint32_t)p[2 * i] | ((uint32_t)p[2 * i + 1] << 16);
-            }
-        }
-    }
-
-#pragma unroll
-    for (uint32_t u = 0; u < kRowUnroll; u++) {
-        const uint32_t o = o0 + u * kRowThreads;
-        uint32_t m = 0;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t a = w[u][i] & 0x7FFF7FFFu;
-            m = umax(m, umax(a & 0xFFFFu, a >> 16));
-        }
-        m = quad_max(m);  // every lane runs the exchange; out-of-range quads hold zeros
-        const bool finite = m < 0x7F80u;
-        const int e = scale_exp_bf16<F>(finite ? m : 0u);
-        const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
-        uint32_t packed = 0, lo = 0, hi = 0;
-        if constexpr (F == E2M1) {
-            packed = finite ? cvt8_fp4_bf16(w[u], sc) : 0u;
-        } else {
-            const float lim = __builtin_amdgcn_ldexpf(MaxNormal<F>::v, e);
-            lo = cvt4_fp8<F>(bf16_lo(w[u][0]), bf16_hi(w[u][0]), bf16_lo(w[u][1]), bf16_hi(w[u][1]), sc, lim);
-            hi = cvt4_fp8<F>(bf16_lo(w[u][2]), bf16_hi(w[u][2]), bf16_lo(w[u][3]), bf16_hi(w[u][3]), sc, lim);
-            lo = finite ? lo : 0u;
-            hi = finite ? hi : 0u;
-        }
-        if (o < total_oct) {
-            if (F == E2M1) {
-                if (VEC) {
-                    *reinterpret_cast<uint32_t *>(codes + (uint64_t)o * 4) = packed;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; i++) codes[(uint64_t)o * 4 + i] = (uint8_t)(packed >> (8 * i));
-                }
-            } else {
-                if (VEC) {
-                    *reinterpret_cast<uint2 *>(codes + (uint64_t)o * 8) = make_uint2(lo, hi);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        codes[(uint64_t)o * 8 + i] = (uint8_t)(lo >> (8 * i));
-                        codes[(uint64_t)o * 8 + 4 + i] = (uint8_t)(hi >> (8 * i));
-                    }
-                }
-            }
-            if ((threadIdx.x & 3u) == 0) scales[o >> 2] = (uint8_t)(finite ? e + 127 : 0xFF);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Transposed mode, optionally after the rotation.  Lane: 4 columns
-// c0 .. c0+3 of one 32-row block at a time (one 8-byte load per row, each
-// wave instruction reading 512 contiguous bytes of a row), so the block's
-// amax and the rotation's butterflies stay in the lane's registers.  A
-// workgroup covers 256 columns x 8 row blocks, one block per wave.  The codes
-// are staged in LDS and written out afterwards as whole
-// 128-byte (E2M1) or 256-byte (FP8) runs of each output row, and the 8 scale
-// bytes of each output row as one 8-byte store.
-constexpr int kTrColsPerLane = 4;
-constexpr int kTrWaves = 8;
-constexpr int kTrBlocks = 8;   // row blocks per workgroup
-constexpr int kTrCols = 256;   // columns per workgroup
-
-// y = c * H32 * diag(s) * x, stages h = 1, 2, 4, 8, 16, one fp32 rounding per op
-__device__ __forceinline__ void hadamard32(float (&y)[32], uint32_t sign_mask) {
-    if (sign_mask) {
-#pragma unroll
-        for (int i = 0; i < 32; i++) y[i] = __uint_as_float(__float_as_uint(y[i]) ^ (((sign_mask >> i) & 1u) << 31));
-    }
-#pragma unroll
-    for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-        for (int j = 0; j < 32; j++) {
-            if (!(j & h)) {
-                const float a = y[j], b = y[j + h];
-                y[j] = __fadd_rn(a, b);
-                y[j + h] = __fsub_rn(a, b);
-            }
-        }
-    }
-    const float c = __uint_as_float(0x3E3504F3u);  // RN_fp32(1/sqrt(32))
-#pragma unroll
-    for (int i = 0; i < 32; i++) y[i] = __fmul_rn(y[i], c);
-}
-
-template <int F, bool ROTATE, bool VEC>
-__global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
-    const uint16_t *__restrict__ x, int64_t ldx, int64_t rows, int64_t cols, uint32_t sign_mask,
-    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
-    constexpr int BB = F == E2M1 ? 16 : 32;             // code bytes per block of one output row
-    constexpr int CB = kTrBlocks * BB;                  // staged bytes per output row: 128 or 256
-    constexpr int NCH = CB / 16;                        // 16-byte chunks per output row
-    __shared__ __attribute__((aligned(16))) uint8_t sC[kTrCols * CB];
-    __shared__ __attribute__((aligned(8))) uint8_t sS[kTrCols * kTrBlocks];
-    // chunk q of output row c sits at c * CB + ((q ^ key(c)) << 4): the 16
-    // lanes of one LDS write pass hold columns 4L + j, whose keys differ
-    const auto key = [](int c) { return (c >> 2) & (NCH - 1); };
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t ctile = (int64_t)blockIdx.x * kTrCols;
-    const int64_t rb0 = (int64_t)blockIdx.y * kTrBlocks;
-    const int64_t nrb = rows / 32;
-    const int nb = (int)((nrb - rb0) < kTrBlocks ? (nrb - rb0) : kTrBlocks);    // valid blocks
-    const int nc = (int)((cols - ctile) < kTrCols ? (cols - ctile) : kTrCols);  // valid columns
-    const int cl = lane * kTrColsPerLane;                                        // lane's first column in the tile
-    const int ncols = nc - cl < kTrColsPerLane ? (nc - cl < 0 ? 0 : nc - cl) : kTrColsPerLane;
-
-    static_assert(kTrWaves == kTrBlocks, "one block per wave");
-    const int b = wave;  // block within the workgroup
-    if (b < nb && ncols > 0) {  // the barrier below is reached by every wave
-        const int64_t rb = rb0 + b;
-        // w[i][0] = columns c0, c0+1 of row 32 rb + i; w[i][1] = columns c0+2, c0+3
-        uint32_t w[32][2];
-        const uint16_t *p = x + rb * 32 * ldx + ctile + cl;
-        if (VEC && ncols == kTrColsPerLane) {
-#pragma unroll
-            for (int i = 0; i < 32; i++) {
-                const uint2 t = *reinterpret_cast<const uint2 *>(p + i * ldx);
-                w[i][0] = t.x;
-                w[i][1] = t.y;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; i++) {
-                uint32_t v[4];
-#pragma unroll
-                for (int j = 0; j < 4; j++) v[j] = j < ncols ? p[i * ldx + j] : 0u;
-                w[i][0] = v[0] | (v[1] << 16);
-                w[i][1] = v[2] | (v[3] << 16);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kTrColsPerLane; j++) {
-            if (j >= ncols) break;
-            float y[32];
-#pragma unroll
-            for (int i = 0; i < 32; i++) y[i] = (j & 1) ? bf16_hi(w[i][j >> 1]) : bf16_lo(w[i][j >> 1]);
-            if (ROTATE) hadamard32(y, sign_mask);
-            uint32_t m = 0;
-#pragma unroll
-            for (int i = 0; i < 32; i++) m = umax(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
-            // bf16 inputs are exact in fp32, so the fp32 scale rule gives the bf16 one
-            const bool finite = m < 0x7F800000u;
-            const int e = scale_exp_f32<F>(finite ? m : 0u);
-            const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
-            const int c = cl + j;
-            if constexpr (F == E2M1) {
-                uint32_t q[4];
-#pragma unroll
-                for (int k = 0; k < 4; k++) q[k] = finite ? cvt8_fp4(y + 8 * k, sc) : 0u;
-                *reinterpret_cast<uint4 *>(&sC[c * CB + ((b ^ key(c)) << 4)]) = make_uint4(q[0], q[1], q[2], q[3]);
-            } else {
-                const float lim = __builtin_amdgcn_ldexpf(MaxNormal<F>::v, e);
-                uint32_t q[8];
-#pragma unroll
-                for (int k = 0; k < 8; k++) {
-                    const uint32_t v = cvt4_fp8<F>(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3], sc, lim);
-                    q[k] = finite ? v : 0u;
-                }
-                *reinterpret_cast<uint4 *>(&sC[c * CB + (((2 * b) ^ key(c)) << 4)]) = make_uint4(q[0], q[1], q[2], q[3]);
-                *reinterpret_cast<uint4 *>(&sC[c * CB + (((2 * b + 1) ^ key(c)) << 4)]) = make_uint4(q[4], q[5], q[6], q[7]);
-            }
-            sS[c * kTrBlocks + b] = (uint8_t)(finite ? e + 127 : 0xFF);
-        }
-    }
-    __syncthreads();
-
-    // write-out: thread t copies chunk t % NCH of output row t / NCH (+ 256 / NCH per step)
-    const int64_t row_bytes = (F == E2M1) ? rows / 2 : rows;
-    const int vchunks = nb * BB / 16;                   // valid chunks per output row
-#pragma unroll
-    for (int k = 0; k < kTrCols * NCH / (64 * kTrWaves); k++) {
-        const int t = k * 64 * kTrWaves + threadIdx.x;
-        const int c = t / NCH, q = t % NCH;
-        if (c >= nc || q >= vchunks) continue;
-        const uint4 v = *reinterpret_cast<const uint4 *>(&sC[c * CB + ((q ^ key(c)) << 4)]);
-        uint8_t *dst = codes + (ctile + c) * row_bytes + rb0 * BB + q * 16;
-        if (VEC) {
-            *reinterpret_cast<uint4 *>(dst) = v;
-        } else {
-            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 16; i++) dst[i] = (uint8_t)(vv[i >> 2] >> (8 * (i & 3)));
-        }
-    }
-    {
-        const int c = threadIdx.x;  // one output row's 8 scale bytes per thread
-        if (c < nc) {
-            uint8_t *dst = scales + (ctile + c) * nrb + rb0;
-            if (nb == kTrBlocks && (((uintptr_t)dst & 7) == 0)) {
-                *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(&sS[c * kTrBlocks]);
-            } else {
-                for (int i = 0; i < nb; i++) dst[i] = sS[c * kTrBlocks + i];
-            }
-        }
-    }
-}
 
 template <int F>
 hipError_t launch_rows_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint8_t *codes,

@@ -1,0 +1,121 @@
+"""The C-ABI library on the host: it loads, exports every function include/mx.h
+declares, and rejects bad arguments before any HIP call (so these checks
+need no GPU; pointer arguments are only compared, never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mx.h")
+
+OK, INVALID, UNSUPPORTED, HIPERR = 0, 1, 2, 3
+E4M3, E5M2, E2M1 = 0, 1, 2
+P, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+
+
+@pytest.fixture(scope="module")
+def L():
+    from precision_block_amax_amd import build as libbuild
+    if not os.path.exists(libbuild.LIB_PATH):
+        libbuild.build()
+    lib = ctypes.CDLL(libbuild.LIB_PATH)
+    lib.mx_quantize.argtypes = [P, i64, i64, i64, i32, P, P, P]
+    lib.mx_quantize_transpose.argtypes = [P, i64, i64, i64, i32, P, P, P]
+    lib.mx_hadamard32_quantize.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
+    lib.mx_quantize_dual.argtypes = [P, i64, i64, i64, i32, P, P, i32, i32, u32, P, P, P]
+    lib.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
+    lib.mx_status_string.argtypes = [ctypes.c_int]
+    lib.mx_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mx_status_t|const char \*|int)\s*\*?\s*(mx_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert {"mx_quantize", "mx_quantize_transpose", "mx_hadamard32_quantize", "mx_quantize_dual",
+            "mx_gemm", "mx_status_string", "mx_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), "libmx.so does not export %s" % n
+
+
+def test_version_and_status_strings(L):
+    assert L.mx_version() == 100
+    for code, name in [(OK, b"MX_OK"), (INVALID, b"MX_ERR_INVALID_ARG"), (UNSUPPORTED, b"MX_ERR_UNSUPPORTED"),
+                       (HIPERR, b"MX_ERR_HIP"), (99, b"MX_ERR_UNKNOWN")]:
+        assert L.mx_status_string(code) == name
+
+
+X, C, S, C2, S2 = (P(a) for a in (0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000))
+
+
+@pytest.mark.parametrize("fn", ["mx_quantize", "mx_quantize_transpose"])
+def test_quantize_rejects(L, fn):
+    f = getattr(L, fn)
+    blocked_rows = fn != "mx_quantize"
+    good_r, good_c = (64, 3) if blocked_rows else (3, 64)
+    assert f(X, -1, 64, 64, E4M3, C, S, None) == INVALID                       # negative size
+    assert f(X, good_r, good_c, good_c, 7, C, S, None) == INVALID              # unknown format
+    bad_r, bad_c = (33, 3) if blocked_rows else (3, 33)
+    assert f(X, bad_r, bad_c, bad_c, E4M3, C, S, None) == INVALID              # blocked dim % 32
+    assert f(X, good_r, good_c, good_c - 1, E4M3, C, S, None) == INVALID      # ldx < cols
+    assert f(None, good_r, good_c, good_c, E4M3, C, S, None) == INVALID        # NULL input
+    assert f(X, good_r, good_c, good_c, E4M3, None, S, None) == INVALID        # NULL codes
+    assert f(X, good_r, good_c, good_c, E4M3, X, S, None) == INVALID           # codes overlap x
+    assert f(X, good_r, good_c, good_c, E4M3, C, P(0x20000010), None) == INVALID  # scales overlap codes
+    assert f(None, 0, good_c, good_c, E4M3, None, None, None) == OK            # empty call
+    assert f(None, good_r, 0, max(good_c, 0), E4M3, None, None, None) == OK
+
+
+def test_hadamard_rejects(L):
+    f = L.mx_hadamard32_quantize
+    assert f(X, 33, 4, 4, 0, E2M1, C, S, None) == INVALID
+    assert f(X, 64, 4, 4, 0x9E3779B9, 5, C, S, None) == INVALID
+    assert f(X, 64, 4, 3, 0, E2M1, C, S, None) == INVALID
+    assert f(None, 0, 4, 4, 0, E2M1, None, None, None) == OK
+
+
+def test_dual_rejects(L):
+    f = L.mx_quantize_dual
+    args = lambda **k: [k.get("x", X), k.get("rows", 64), k.get("cols", 64), k.get("ldx", 64), k.get("fr", E4M3),
+                        k.get("cr", C), k.get("sr", S), k.get("ft", E2M1), k.get("rot", 1), 0, k.get("ct", C2),
+                        k.get("st", S2), None]
+    assert f(*args(rot=2)) == INVALID                    # rotate is 0 or 1
+    assert f(*args(rows=48)) == INVALID                  # rows % 32 (transposed form)
+    assert f(*args(cols=48, ldx=48)) == INVALID          # cols % 32 (row form)
+    assert f(*args(ft=9)) == INVALID
+    assert f(*args(ct=C)) == INVALID                     # the two code buffers overlap
+    assert f(*args(st=P(0x30000040))) == INVALID         # scale buffers overlap
+    assert f(*args(sr=P(0x40000000))) == INVALID         # row scales inside the transposed codes
+    assert f(*args(ldx=63)) == INVALID
+    assert f(*args(x=None)) == INVALID
+    assert f(*args(rows=0, x=None, cr=None, sr=None, ct=None, st=None)) == OK
+
+
+def test_gemm_rejects(L):
+    f = L.mx_gemm
+    A, AS, B, BS, Cc = (P(a) for a in (0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000))
+    assert f(A, AS, E4M3, B, BS, E4M3, 64, 64, 48, Cc, 0, 64, None) == INVALID   # K % 32
+    assert f(A, AS, E4M3, B, BS, E4M3, -1, 64, 64, Cc, 0, 64, None) == INVALID
+    assert f(A, AS, E4M3, B, BS, 3, 64, 64, 64, Cc, 0, 64, None) == INVALID     # format
+    assert f(A, AS, E4M3, B, BS, E4M3, 64, 64, 64, Cc, 2, 64, None) == INVALID  # output type
+    assert f(A, AS, E4M3, B, BS, E4M3, 64, 64, 64, Cc, 0, 63, None) == INVALID  # ldc < N
+    assert f(A, AS, E4M3, B, BS, E4M3, 64, 64, 64, None, 0, 64, None) == INVALID
+    assert f(None, AS, E4M3, B, BS, E4M3, 64, 64, 64, Cc, 0, 64, None) == INVALID
+    assert f(A, AS, E4M3, B, BS, E4M3, 64, 64, 64, P(0x10000100), 0, 64, None) == INVALID  # C overlaps A
+    assert f(None, None, E4M3, None, None, E4M3, 0, 64, 64, None, 0, 64, None) == OK       # empty
+
+
+def test_valid_call_without_a_device_reports_hip_error(L):
+    """past validation the library asks HIP for the device; without one it
+    returns MX_ERR_HIP instead of crashing (on a GPU machine this would launch,
+    so it is skipped there)"""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the launch path is covered by the GPU tests")
+    assert L.mx_quantize(X, 4, 64, 64, E4M3, C, S, None) == HIPERR

@@ -286,3 +286,70 @@ def test_every_bf16_at_every_scale(mx, fmt):
     _cmp(mx.quantize_transpose(to_dev_bf16(xt), fmt), oracle.quantize_transpose(xt, fmt),
          "transposed, every bf16 x every e")
     assert np.array_equal(oracle.quantize_transpose(xt, fmt)[0], want[0])
+
+
+# ---------------------------------------------------------------------------
+# Fused dual-direction quantizer: both outputs equal the single-direction oracle forms.
+
+def _cmp_dual(got, x, fr, ft, rotate, mask, what):
+    _cmp(got[:2], oracle.quantize(x, fr), what + " (row form)")
+    want_t = oracle.hadamard32_quantize(x, ft, mask) if rotate else oracle.quantize_transpose(x, ft)
+    _cmp(got[2:], want_t, what + " (transposed form)")
+
+
+DUAL_CASES = [(1, "X", "e4m3", "e4m3", False, 0), (2, "W", "e2m1", "e2m1", False, 0),
+              (3, "dY", "e2m1", "e2m1", True, 0), (3, "X", "e2m1", "e2m1", True, 0x9E3779B9),
+              (0, "A", "e5m2", "e4m3", True, 0xFFFFFFFF)]
+
+
+@pytest.mark.parametrize("ci,name,fr,ft,rotate,mask", DUAL_CASES)
+def test_dual_workloads(mx, ci, name, fr, ft, rotate, mask):
+    cfg = workloads.config(ci)
+    x = workloads.draw_tensor(cfg, name)
+    print("case dual", cfg.name, name, fr, ft, rotate, hex(mask), x.shape, flush=True)
+    got = mx.quantize_dual(to_dev_bf16(x), fr, ft, rotate, mask)
+    _cmp_dual(got, x, fr, ft, rotate, mask, "%s/%s" % (cfg.name, name))
+
+
+@pytest.mark.parametrize("fr", FMTS)
+@pytest.mark.parametrize("ft", FMTS)
+@pytest.mark.parametrize("rotate", [False, True])
+def test_dual_format_pairs_ragged(mx, fr, ft, rotate):
+    """rows and columns not multiples of the workgroup tile (256 x 256)"""
+    rng = np.random.default_rng(FMTS.index(fr) * 3 + FMTS.index(ft))
+    x = _rand_bits(96 + 32 * FMTS.index(fr), 352 - 32 * FMTS.index(ft), int(rng.integers(1 << 30)))
+    mask = 0x9E3779B9 if rotate else 0
+    _cmp_dual(mx.quantize_dual(to_dev_bf16(x), fr, ft, rotate, mask), x, fr, ft, rotate, mask, "ragged")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dual_edges_strided_unaligned(mx, fmt):
+    import torch
+    rows_e = edge_rows(64, 256)     # special values along rows
+    cols_e = edge_cols(256, 64)     # ... and along columns
+    x = np.concatenate([np.concatenate([rows_e, np.zeros((64, 0), np.uint16)], axis=1)[:, :64], cols_e[:64]], axis=0)
+    x = np.ascontiguousarray(np.concatenate([x, edge_rows(128, 64)], axis=1)[:, :96])
+    _cmp_dual(mx.quantize_dual(to_dev_bf16(x), fmt, fmt, True, 0x12345678), x, fmt, fmt, True, 0x12345678, "edges")
+    # strided input (ldx > cols) and misaligned outputs (byte-store path)
+    big = _rand_bits(128, 200, 11)
+    xs = to_dev_bf16(big)[:, 8:168]
+    rows, cols = xs.shape
+    raw = torch.empty(4 * rows * cols + 64, dtype=torch.uint8, device="cuda")
+    cb = mx.code_cols(cols, fmt) * rows
+    ctb = mx.code_cols(rows, fmt) * cols
+    off = 1
+    cr = raw[off:off + cb].view(rows, -1)
+    sr = raw[off + cb:off + cb + rows * cols // 32].view(rows, -1)
+    o2 = off + cb + rows * cols // 32 + 3
+    ct = raw[o2:o2 + ctb].view(cols, -1)
+    st = raw[o2 + ctb:o2 + ctb + rows * cols // 32].view(cols, -1)
+    got = mx.quantize_dual(xs, fmt, fmt, False, 0, out=(cr, sr, ct, st))
+    _cmp_dual(got, np.ascontiguousarray(big[:, 8:168]), fmt, fmt, False, 0, "strided/unaligned")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dual_every_bf16_at_every_scale(mx, fmt):
+    x = exhaustive_blocks(fmt)
+    x = np.concatenate([x, np.zeros((-x.shape[0] % 32, x.shape[1]), np.uint16)])   # rows to a multiple of 32
+    got = mx.quantize_dual(to_dev_bf16(x), fmt, fmt, False, 0)
+    _cmp_dual(got, x, fmt, fmt, False, 0, "dual, every bf16 x every e")
