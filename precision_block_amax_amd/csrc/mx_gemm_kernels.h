@@ -957,7 +957,12 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                 const int gm = mbase + pass * PASS_ROWS + m, gn = nbase + c * (16 / ESZ);
                 if (gm >= g.M) continue;
                 if (vec) {
-                    *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(g.c) + ((int64_t)gm * g.ldc + gn) * ESZ) = t;
+                    // non-temporal: C is not read again by this kernel, and the lines should not
+                    // linger dirty in the last-level cache for the next kernel to write back
+                    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                    __builtin_nontemporal_store(
+                        u32x4{t.x, t.y, t.z, t.w},
+                        reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(g.c) + ((int64_t)gm * g.ldc + gn) * ESZ));
                 } else {
                     const uint32_t w4[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
