@@ -212,16 +212,31 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, command: 
     copy = [k for k in f_kib if "copyBuffer" in k or "copy" in k.lower()]
     if not copy:
         raise RuntimeError("no copy kernel in the counter passes (run bench.py with --calibrate-copy)")
+
+    def largest_copy(rows):
+        # the 256 MiB calibration copy is the largest copy dispatch (torch also launches tiny copies)
+        per = {}
+        for r in rows:
+            if r["Kernel_Name"] in copy:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return max(per.values())
+
     known_kib = 256 * 1024.0
-    f_scale, w_scale = known_kib / f_kib[copy[0]], known_kib / w_kib[copy[0]]
+    f_copy, w_copy = largest_copy(fetch), largest_copy(write)
+    f_scale, w_scale = known_kib / f_copy, known_kib / w_copy
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     lines = ["# rocprofv3 kernel trace: %s" % WORKLOAD, "",
              "Command (from the repository root on the GPU box):", "", "    " + command[0], "",
+             "The library's kernels only (torch's kernels that fill the cache before each lone launch, "
+             "and its copies, are left out; share is of the library's kernel time). Calls count the "
+             "launches inside the step and the lone launches after a clean cache fill.", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+    mine = [r for r in stats if "mx::" in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in mine) or 1.0
+    for r in sorted(mine, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
             r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+            float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / total))
     with open(os.path.join(ROOT, "profiles", "kernel_trace_%s.md" % WORKLOAD), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -231,7 +246,8 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, command: 
              "    " + command[1], "    " + command[2], "",
              "Calibration: a plain 256 MiB device copy (`%s`) reads FETCH_SIZE = %.0f KiB and "
              "WRITE_SIZE = %.0f KiB per dispatch for 262144 KiB read and written, so counter KiB are "
-             "scaled by %.4f (fetch) and %.4f (write)." % (copy[0], f_kib[copy[0]], w_kib[copy[0]], f_scale, w_scale),
+             "scaled by %.4f (fetch) and %.4f (write). Kernels called at several sizes (the row "
+             "quantizers) show the mean over their calls." % (copy[0], f_copy, w_copy, f_scale, w_scale),
              "", "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (MB) | written (MB) |", "|---|---|---|---|---|"]
     for k in f_kib:
         if k in copy or "mx::" not in k:
