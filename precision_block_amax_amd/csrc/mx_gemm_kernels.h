@@ -525,6 +525,22 @@ __device__ __forceinline__ void barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// tile hand-over mark between the carrier's fast and exact kernels (see there)
+constexpr uint16_t kMarkBf16 = 0x7FBE;      // bf16 NaN, quiet bit clear: bf16_rne never yields it
+constexpr uint32_t kMarkF32 = 0x7FBADBADu;  // fp32 NaN, quiet bit clear: arithmetic never yields it
+template <bool BF16OUT>
+__device__ __forceinline__ void mark_tile(const GemmArgs &g, int m0, int n0) {
+    const int64_t i = (int64_t)m0 * g.ldc + n0;
+    if constexpr (BF16OUT) reinterpret_cast<uint16_t *>(g.c)[i] = kMarkBf16;
+    else reinterpret_cast<uint32_t *>(g.c)[i] = kMarkF32;
+}
+template <bool BF16OUT>
+__device__ __forceinline__ bool tile_marked(const GemmArgs &g, int m0, int n0) {
+    const int64_t i = (int64_t)m0 * g.ldc + n0;
+    if constexpr (BF16OUT) return reinterpret_cast<const uint16_t *>(g.c)[i] == kMarkBf16;
+    else return reinterpret_cast<const uint32_t *>(g.c)[i] == kMarkF32;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -669,8 +685,17 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     const v4i rSB = rsrc(g.bs + (int64_t)n0 * kblocks, nrecSB);
 
     // carrier: reference scale per row and the tile's path (threads 0..255:
-    // rows of A, 256..511: rows of B)
-    if constexpr (MODE != 0) {
+    // rows of A, 256..511: rows of B).  The fast kernel (MODE 1) leaves a tile
+    // whose rows' scales spread too far (or hold 0xFF) to the exact per-block
+    // kernel (MODE 2) and marks it with a sentinel in C[m0][n0] that no result
+    // store produces (a NaN with its quiet bit clear); the exact kernel, which
+    // runs next on the same stream, reads that one element instead of every
+    // scale of the tile.  A false match would only make it recompute a tile,
+    // exactly.
+    if constexpr (MODE == 2) {
+        if (!tile_marked<BF16OUT>(g, m0, n0)) return;  // uniform across the workgroup
+    }
+    if constexpr (MODE == 1) {
         const bool isA = tid < BM;
         const int r = isA ? tid : tid - BM;
         const int gr = isA ? min(m0 + r, g.M - 1) : min(n0 + r, g.N - 1);
@@ -679,8 +704,10 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
         row_scale_range((isA ? g.as : g.bs) + (int64_t)gr * kblocks, kblocks, vec, mx_, mn_);
         (isA ? sRa : sRb)[r] = mx_;
         const bool w = mx_ - mn_ > kSpreadMax || mx_ == 255;
-        const bool wide = __syncthreads_or(w) != 0;
-        if (wide != (MODE == 2)) return;  // uniform across the workgroup
+        if (__syncthreads_or(w) != 0) {  // uniform across the workgroup
+            if (tid == 0) mark_tile<BF16OUT>(g, m0, n0);
+            return;
+        }
     }
 
     // per-lane DMA source offsets, constant along K: lane l of instruction q
