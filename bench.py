@@ -374,6 +374,24 @@ def main() -> int:
                   "frac_of_hbm_peak": round(dual_bytes / (t_dual * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                   "separate_ms": round(t_row + t_rot, 4), "speedup": round((t_row + t_rot) / t_dual, 3)}
     del dy, outs, r_out, t_out
+
+    # One rank's share of an FSDP2 MXFP8 weight all-gather: quantize its slab
+    # of gate/up weight rows (1/8 of dim 0) to E4M3; the payload it
+    # contributes to the gather is codes + scales instead of bf16.
+    cfg2 = workloads.config(2)
+    wfull = workloads.draw_tensor(cfg2, "W", seed=args.seed)
+    slab_rows = wfull.shape[0] // 8
+    slab = torch.from_numpy(wfull[:slab_rows].view(np.int16)).view(torch.bfloat16).to("cuda")
+    del wfull
+    so = mx.quantize(slab, "e4m3")
+    t_slab = alone(lambda: mx.quantize(slab, "e4m3", out=so))
+    nb = slab.numel()
+    fsdp_shard = {"slab": "%s/W rows 0..%d of %d (one of 8 ranks)" % (cfg2.name, slab_rows, slab_rows * 8),
+                  "format": "e4m3", "ms": round(t_slab, 4),
+                  "GBps": round(quant_bytes(slab_rows, slab.shape[1], "e4m3") / (t_slab * 1e-3) / 1e9, 1),
+                  "gather_bytes": nb * (1 + 1.0 / 32), "gather_bytes_bf16": nb * 2.0,
+                  "gather_ratio": round((1 + 1.0 / 32) / 2.0, 4)}
+    del slab, so
     del flush
 
     if args.calibrate_copy:
@@ -422,6 +440,7 @@ def main() -> int:
         "quantize_GBps": round(quant_gbps, 1), "quantize_frac_of_hbm_peak": round(quant_gbps / PEAK_HBM_GBPS, 4),
         "quantize_GBps_isolated": round(quant_gbps_iso, 1),
         "fused_dual": fused_dual,
+        "fsdp_shard": fsdp_shard,
         "quantize_frac_of_hbm_peak_isolated": round(quant_gbps_iso / PEAK_HBM_GBPS, 4),
         "kernels": [{kk: (round(v, 4) if isinstance(v, float) else
                           {a: round(b, 4) for a, b in v.items()} if isinstance(v, dict) else v)
@@ -439,6 +458,9 @@ def main() -> int:
         print("fused dual quantize (%s, %s): %.1f us alone, %.1f%% of HBM; the two single calls: %.1f us" % (
             fused_dual["tensor"], fused_dual["formats"], fused_dual["ms"] * 1e3, 100 * fused_dual["frac_of_hbm_peak"],
             fused_dual["separate_ms"] * 1e3), file=sys.stderr)
+        print("fsdp2 shard quantize (%s, e4m3): %.1f us alone, %.0f GB/s; gather payload %.3fx of bf16" % (
+            fsdp_shard["slab"], fsdp_shard["ms"] * 1e3, fsdp_shard["GBps"], fsdp_shard["gather_ratio"]),
+            file=sys.stderr)
     print(json.dumps(line), flush=True)
     return 0
 
