@@ -263,6 +263,44 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, command: 
 
 
 # the kernel symbol each bench launch name runs (dominant kernel lookup in traffic.json)
+def ablation(mx, torch, seed: int) -> dict:
+    """Numerical proxy for the weight-gradient recipe (FP4-training article
+    on hzrcw.cc, sections 02-03): dW = dY^T X over 8192 tokens with dY
+    heavy-tailed (1e-3 * Student-t, nu = 3, as the down-projection gradient)
+    and X ~ N(0, 1), through the library's quantizers and GEMM, against the
+    fp64 product of the same bf16 inputs.  Relative Frobenius error of:
+    MXFP4 without rotation, with the fixed-sign rotation (two masks), with
+    random signs drawn anew for each of 8 steps, and MXFP8 without rotation.
+    Stochastic rounding is not built."""
+    cfg = workloads.config(3)
+    dy = workloads.draw_tensor(cfg, "dY", seed=seed)[:, :1024]
+    x = workloads.draw_tensor(cfg, "X", seed=seed)[:, :512]
+    f64 = lambda b: workloads.bf16_bits_to_f32(b).astype(np.float64)
+    ref = f64(dy).T @ f64(x)
+    nref = np.linalg.norm(ref)
+    dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to("cuda")
+    dyd, xd = dev(dy), dev(x)
+
+    def dw(qa, qb, fmt):
+        c = mx.gemm(qa[0], qa[1], fmt, qb[0], qb[1], fmt, out_dtype=torch.float32)
+        return float(np.linalg.norm(c.cpu().numpy().astype(np.float64) - ref) / nref)
+
+    out = {"shape": "dW[1024x512] = dY[8192x1024]^T X[8192x512]", "metric": "||dW - dW_fp64||_F / ||dW_fp64||_F"}
+    out["mxfp4_no_rotation"] = dw(mx.quantize_transpose(dyd, "e2m1"), mx.quantize_transpose(xd, "e2m1"), "e2m1")
+    for mask in (0, 0x9E3779B9):
+        out["mxfp4_fixed_rotation_mask_%08x" % mask] = dw(mx.hadamard32_quantize(dyd, "e2m1", mask),
+                                                          mx.hadamard32_quantize(xd, "e2m1", mask), "e2m1")
+    rng = np.random.default_rng(seed + 1)
+    errs = []
+    for _ in range(8):
+        mask = int(rng.integers(0, 1 << 32))
+        errs.append(dw(mx.hadamard32_quantize(dyd, "e2m1", mask), mx.hadamard32_quantize(xd, "e2m1", mask), "e2m1"))
+    out["mxfp4_random_sign_rotation_8_steps"] = {"mean": float(np.mean(errs)), "min": float(np.min(errs)),
+                                                 "max": float(np.max(errs))}
+    out["mxfp8_e4m3_no_rotation"] = dw(mx.quantize_transpose(dyd, "e4m3"), mx.quantize_transpose(xd, "e4m3"), "e4m3")
+    return out
+
+
 def kernel_symbol(name: str) -> str:
     fa, fb = None, None
     if "mx_gemm" in name:
@@ -283,6 +321,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=workloads.DEFAULT_SEED)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table to stderr")
+    ap.add_argument("--ablation", action="store_true",
+                    help="only the weight-gradient rotation ablation (dW error of the Wgrad recipes)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -303,6 +343,10 @@ def main() -> int:
         return 2
     mx.lib()
     torch.cuda.set_device(0)
+
+    if args.ablation:
+        print(json.dumps({"ablation": ablation(mx, torch, args.seed)}), flush=True)
+        return 0
 
     print("bench: building inputs", file=sys.stderr, flush=True)
     step = Step(mx, torch, args.seed)
