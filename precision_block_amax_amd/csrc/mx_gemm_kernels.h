@@ -561,22 +561,6 @@ __device__ __forceinline__ v4i rsrc(const void *base, uint32_t bytes) {
 // would then wait for every load in flight before an LDS read, stays out of
 // it: the kernel waits for the loads explicitly (vmcnt) before its barriers.
 // M0 carries the LDS address and needs one wait state before the load.
-// 4 bytes per lane for the lanes in `mask` only (EXEC is set and restored
-// inside the statement, so no branch splits the caller's code).
-// The mask halves must be wave-uniform; they go through readfirstlane so
-// the compiler keeps them in scalar registers.
-__device__ __forceinline__ void dma4_masked(v4i r, void *lds, int voff, int soff, uint64_t mask) {
-    const uint32_t m = (uint32_t)(uintptr_t)(lds_t)lds;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)mask);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(mask >> 32));
-    uint64_t saved;
-    asm volatile(
-        "s_mov_b64 %0, exec\n\ts_mov_b32 exec_lo, %5\n\ts_mov_b32 exec_hi, %6\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-        "buffer_load_dword %1, %3, %4 offen lds\n\ts_mov_b64 exec, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(m), "s"(r), "s"(soff), "s"(lo), "s"(hi)
-        : "memory", "m0");
-}
 __device__ __forceinline__ void dma16(v4i r, void *lds, int voff, int soff) {
     const uint32_t m = (uint32_t)(uintptr_t)(lds_t)lds;
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
@@ -661,7 +645,6 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint8_t sB0[BN * RBB], sB1[BN * RBB];
     __shared__ __attribute__((aligned(16))) uint8_t sS0[2][BM * 16], sS1[2][BM * 16];  // [A, B][row * 16 + byte]
     __shared__ int sRa[BM], sRb[BN];
-    __shared__ __attribute__((aligned(16))) uint8_t sPF[256];  // landing area of the L2 prefetches, never read
     auto stA = [&](auto S) -> uint8_t * { if constexpr (decltype(S)::value == 0) return sA0; else return sA1; };
     auto stB = [&](auto S) -> uint8_t * { if constexpr (decltype(S)::value == 0) return sB0; else return sB1; };
     auto stS = [&](auto T, int op) -> uint8_t * { if constexpr (decltype(T)::value == 0) return sS0[op]; else return sS1[op]; };
@@ -726,23 +709,6 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     const int voffB = rowB0 * rowB + (((lane % CPRB) ^ swz_key<RBB>(rowB0)) << 4);
     const int voffA1 = RBA == 128 ? (voffA ^ 64) : voffA, voffB1 = RBB == 128 ? (voffB ^ 64) : voffB;
 
-    // L2 prefetch two stages ahead of the stage loads: every wave issues one
-    // 4-byte-per-lane load per stage (one lane per 128-byte row line), so the
-    // barrier can wait for all but the newest load.  Tiles running side by
-    // side on an XCD (eight tile rows by four tile columns) share rows, so
-    // each touches only its share: a quarter of its A rows, picked by its
-    // column index (first half of the loading waves), and an eighth of its B
-    // rows, picked by its row index (second half).
-    constexpr int PFA = 64 / (NWD / 2), PFB = 32 / (NWD / 2);  // rows per prefetching wave
-    const bool pfB = dw >= NWD / 2;
-    const int pw = dw & (NWD / 2 - 1);
-    const int pf_row0 = pfB ? 32 * ((m0 / BM) & 7) + pw * PFB : 64 * ((n0 / BN) & 3) + pw * PFA;
-    const int pf_voff = (pf_row0 + lane) * (pfB ? rowB : rowA);
-    const uint64_t pf_mask = pfB ? (1ull << PFB) - 1 : (1ull << PFA) - 1;
-    const v4i rPF = pfB ? rB : rA;
-    const int pf_step = pfB ? RBB : RBA;
-    const int pf_nrec = (int)(pfB ? nrecB : nrecA);
-
     // scale slot loads: eight 64-row instructions (four for A's rows, four
     // for B's), NSI per loading wave; 16 bytes of each row, one line per row
     constexpr int NSI = 8 / NWD;
@@ -771,7 +737,6 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                 dma16(sop ? rSB : rSA, stS(T, sop) + (srow0 + 64 * u) * 16, svoff + 64 * u * kblocks,
                       live ? kt * SBY : (int)(sop ? nrecSB : nrecSA));
         }
-        dma4_masked(rPF, sPF, pf_voff, kt + 2 < ntk ? (kt + 2) * pf_step : pf_nrec, pf_mask);
     };
 
     v16f acc[4][2];  // acc[i][j]: C^T tile of A rows i, B rows j
@@ -914,7 +879,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
         static_for<0, 2 * SPS>([&](auto uu) {
             constexpr int u = decltype(uu)::value;
             const int kt = kt0 + u;  // stage computed in this step
-            wait_vm<1>();  // this stage's loads; the newest (the prefetch) may still run
+            wait_vm<0>();  // this stage's loads
             barrier();
             issue(std::integral_constant<int, (u + 1) % 2>{}, std::integral_constant<int, ((u + 1) / SPS) % 2>{},
                   std::integral_constant<bool, (u + 1) % SPS == 0>{}, kt + 1);
