@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_hadamard_c.restype = ctypes.c_float
         L.oracle_hadamard32_f32.argtypes = [P, u32, P]
         L.oracle_hadamard32_f32.restype = None
+        L.oracle_philox4x32_10.argtypes = [P, P, P]
+        L.oracle_philox4x32_10.restype = None
         for name, args in {
             "oracle_e8m0_many": [P, i64, i32, P],
             "oracle_cast_many": [P, P, i64, i32, P],
@@ -68,6 +70,9 @@ def lib() -> ctypes.CDLL:
             "oracle_quantize_transpose": [P, i64, i64, i64, i32, P, P],
             "oracle_hadamard32_quantize": [P, i64, i64, i64, u32, i32, P, P],
             "oracle_dequantize": [P, P, i64, i64, i32, P],
+            "oracle_cast_sr_many": [P, P, P, i64, i32, P],
+            "oracle_sr_words": [ctypes.c_uint64, i64, P],
+            "oracle_quantize_transpose_sr": [P, i64, i64, i64, i32, u32, ctypes.c_uint64, i32, P, P],
         }.items():
             fn = getattr(L, name)
             fn.argtypes = args
@@ -120,6 +125,32 @@ def cast(v: np.ndarray, e: np.ndarray, fmt: str) -> np.ndarray:
     return out
 
 
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """one Philox4x32-10 block: four 32-bit counter words, two key words -> four words"""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32).reshape(4)
+    k = np.ascontiguousarray(key, dtype=np.uint32).reshape(2)
+    out = np.empty(4, dtype=np.uint32)
+    lib().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_words(seed: int, n: int) -> np.ndarray:
+    """the random words of output elements 0 .. n-1 under `seed`"""
+    out = np.empty(n, dtype=np.uint32)
+    _check(lib().oracle_sr_words(seed & (2**64 - 1), n, _ptr(out)))
+    return out
+
+
+def cast_sr(v: np.ndarray, e: np.ndarray, r: np.ndarray, fmt: str) -> np.ndarray:
+    """stochastically rounded element codes of v * 2^-e with random words r"""
+    v = np.ascontiguousarray(v, dtype=np.float64).ravel()
+    e = np.ascontiguousarray(np.broadcast_to(e, v.shape), dtype=np.int32).ravel()
+    r = np.ascontiguousarray(np.broadcast_to(r, v.shape), dtype=np.uint32).ravel()
+    out = np.empty(v.size, dtype=np.uint8)
+    _check(lib().oracle_cast_sr_many(_ptr(v), _ptr(e), _ptr(r), v.size, FMT_CODES[fmt], _ptr(out)))
+    return out
+
+
 def decode(codes: np.ndarray, fmt: str) -> np.ndarray:
     c = np.ascontiguousarray(codes, dtype=np.uint8).ravel()
     out = np.empty(c.size, dtype=np.float64)
@@ -168,6 +199,18 @@ def hadamard32_quantize(x_bits: np.ndarray, fmt: str, sign_mask: int = 0) -> Tup
     scales = np.empty((cols, rows // 32), dtype=np.uint8)
     _check(lib().oracle_hadamard32_quantize(_ptr(x), rows, cols, cols, sign_mask & 0xFFFFFFFF,
                                             FMT_CODES[fmt], _ptr(codes), _ptr(scales)))
+    return codes, scales
+
+
+def quantize_transpose_sr(x_bits: np.ndarray, fmt: str, seed: int, rotate: bool = False,
+                          sign_mask: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """transposed mode (after the rotation if `rotate`) with stochastic rounding"""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, cols = x.shape
+    codes = np.empty((cols, code_cols(rows, fmt)), dtype=np.uint8)
+    scales = np.empty((cols, rows // 32), dtype=np.uint8)
+    _check(lib().oracle_quantize_transpose_sr(_ptr(x), rows, cols, cols, int(bool(rotate)), sign_mask & 0xFFFFFFFF,
+                                              seed & (2**64 - 1), FMT_CODES[fmt], _ptr(codes), _ptr(scales)))
     return codes, scales
 
 

@@ -32,7 +32,9 @@
  *   - E2M1 packing: element 2i in bits 3:0, element 2i+1 in bits 7:4;
  *   - rotation arithmetic: fp32, one rounding per operation, butterfly
  *     stages h = 1, 2, 4, 8, 16 in that order, each (a, b) -> (a+b, a-b),
- *     then one multiply by c = RN32(1/sqrt 32); no rounding to bf16.
+ *     then one multiply by c = RN32(1/sqrt 32); no rounding to bf16;
+ *   - stochastic rounding (ablation only): the textbook definition taken to
+ *     32 fraction bits, random words from Philox4x32-10 (details below).
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math;
  * SSE arithmetic, so every float operation rounds to float).
@@ -209,8 +211,98 @@ static void hadamard32(float *x, uint32_t mask)
 }
 
 /* ---------------------------------------------------------------------------
+ * Stochastic rounding (the randomised alternative to round-to-nearest that
+ * the FP4-training article, section 01, names among the common fixes it
+ * argues against; the pages give no definition, so this is the textbook one):
+ * with lo <= |q| < hi the two neighbouring magnitudes on the format grid,
+ * |q| goes up to hi with probability (|q| - lo) / (hi - lo), else down to lo.
+ * The probability is taken to 32 fraction bits, F = floor(2^32 (|q|-lo)/(hi-lo)),
+ * and a 32-bit random word r decides: up iff r < F.  Values on the grid never
+ * move; magnitudes at or above the largest normal saturate as in the RNE cast;
+ * the block scale is the RNE path's.
+ *
+ * Random words come from Philox4x32-10, the counter-based generator of
+ * Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2,
+ * 3" (SC 2011): element i of an output array takes word i mod 4 of the block
+ * for counter (i / 4 as two 32-bit words, low first, then 0, 0) and key
+ * (seed low word, seed high word).
+ */
+static void philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; round++) {
+        if (round > 0) { /* key schedule: Weyl sequence */
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t p0 = (uint64_t)0xD2511F53u * x0, p1 = (uint64_t)0xCD9E8D57u * x2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t y0 = hi1 ^ x1 ^ k0, y1 = lo1, y2 = hi0 ^ x3 ^ k1, y3 = lo0;
+        x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+    }
+    out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* random word of element i under a 64-bit seed */
+static uint32_t sr_word(uint64_t i, uint64_t seed)
+{
+    uint32_t ctr[4] = {(uint32_t)(i >> 2), (uint32_t)(i >> 34), 0u, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    philox4x32_10(ctr, key, out);
+    return out[i & 3];
+}
+
+static uint8_t encode_elem_sr(double q, uint32_t r, const orc_fmt *f)
+{
+    int neg = signbit(q) ? 1 : 0;
+    double a = fabs(q), mag;
+    int emin = 1 - f->bias;
+    if (a >= f->maxnorm) {
+        mag = f->maxnorm;
+    } else if (a == 0.0) {
+        mag = 0.0;
+    } else {
+        int k = floor_log2(a);
+        int kk = k < emin ? emin : k;
+        double quantum = ldexp(1.0, kk - f->mbits); /* grid spacing around a */
+        double t = a / quantum;                      /* exact: power-of-two division */
+        double n = floor(t);
+        double F = floor(ldexp(t - n, 32));          /* < 2^32, exact */
+        if ((double)r < F) n += 1.0;
+        mag = n * quantum;
+        if (mag > f->maxnorm) mag = f->maxnorm;
+    }
+    return encode_elem(neg ? -mag : mag, f); /* mag is on the grid: no further rounding */
+}
+
+/* ---------------------------------------------------------------------------
  * exported API.  Return 0 on success, -1 on a bad argument.
  */
+
+void oracle_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out)
+{
+    philox4x32_10(ctr, key, out);
+}
+
+/* stochastically rounded element codes of v[i] * 2^-e[i] with random words r[i] */
+int oracle_cast_sr_many(const double *v, const int32_t *e, const uint32_t *r, int64_t n, int fmt, uint8_t *out)
+{
+    if (!valid_fmt(fmt)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) out[i] = encode_elem_sr(ldexp(v[i], -e[i]), r[i], &FMT[fmt]);
+    return 0;
+}
+
+/* the random words the stochastic-rounding quantizer uses for elements 0 .. n-1 */
+int oracle_sr_words(uint64_t seed, int64_t n, uint32_t *out)
+{
+    if (n < 0) return -1;
+    for (int64_t i = 0; i < n; i++) out[i] = sr_word((uint64_t)i, seed);
+    return 0;
+}
 
 float oracle_hadamard_c(void) { return hadamard_c(); }
 
@@ -344,6 +436,39 @@ int oracle_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
             uint8_t code = (fmt == ORC_E2M1) ? (uint8_t)((k & 1) ? (byte >> 4) : (byte & 0xF)) : byte;
             int S = scales[r * nb + k / 32];
             out[r * cols + k] = (S == 0xFF) ? NAN : ldexp(decode_elem(code, fmt), S - 127);
+        }
+    }
+    return 0;
+}
+
+/* Transposed mode with stochastic rounding, optionally after the rotation:
+ * as oracle_quantize_transpose / oracle_hadamard32_quantize (same blocks, same
+ * scales), but element t of output row c is rounded with the random word of
+ * output index c * rows + t. */
+int oracle_quantize_transpose_sr(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int rotate,
+                                 uint32_t mask, uint64_t seed, int fmt, uint8_t *codes, uint8_t *scales)
+{
+    if (!valid_fmt(fmt) || rows < 0 || cols < 0 || rows % 32 || ldx < cols || (rotate != 0 && rotate != 1))
+        return -1;
+    int64_t nb = rows / 32;
+    const orc_fmt *f = &FMT[fmt];
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; c++) {
+        float t[32];
+        double v[32];
+        uint8_t q[32];
+        for (int64_t b = 0; b < nb; b++) {
+            for (int i = 0; i < 32; i++) t[i] = (float)bf16_value(x[(32 * b + i) * ldx + c]);
+            if (rotate) hadamard32(t, mask);
+            for (int i = 0; i < 32; i++) v[i] = (double)t[i];
+            /* the scale and the non-finite rule of the round-to-nearest path */
+            quantize_block(v, f, q, &scales[c * nb + b]);
+            if (scales[c * nb + b] != 0xFF) {
+                int e = scales[c * nb + b] - 127;
+                for (int i = 0; i < 32; i++)
+                    q[i] = encode_elem_sr(ldexp(v[i], -e), sr_word((uint64_t)(c * rows + 32 * b + i), seed), f);
+            }
+            store_block(q, fmt, codes + c * code_bytes(rows, fmt) + code_bytes(32 * b, fmt));
         }
     }
     return 0;
