@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -43,7 +44,7 @@ CONFIGS = (1, 2, 3)  # the three Llama-3.1-8B workloads
 WORKLOAD = "llama31_8b_linear_set"
 PROFILE_COMMANDS = (
     "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace -- "
-    "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch -- "
     "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write -- "
@@ -237,6 +238,24 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, command: 
         lines.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
             r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / total))
+    # The same dispatches split by phase: every library launch before the first
+    # cache-filling reduction belongs to the warm-up and timed steps (the last
+    # steps/(steps+warmup) of them are timed, as bench.py's events are); the
+    # rest are the lone launches and the extra records.
+    trace = sorted(_read_csv(_find(trace_dir, "kernel_trace.csv")), key=lambda r: int(r["Dispatch_Id"]))
+    first_flush = next((int(r["Dispatch_Id"]) for r in trace if "reduce" in r["Kernel_Name"].lower()), None)
+    steps, warmup = (int(a) for a in re.search(r"--steps (\d+) --warmup (\d+)", command[0]).groups())
+    step_calls = {}
+    for r in trace:
+        if "mx::" in r["Kernel_Name"] and (first_flush is None or int(r["Dispatch_Id"]) < first_flush):
+            step_calls.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "Inside the timed steps only (the launches bench.py's HIP events time; the first "
+              "%d of every %d step launches are warm-up):" % (warmup, steps + warmup), "",
+              "| kernel | timed calls | average (us) |", "|---|---|---|"]
+    for k, d in sorted(step_calls.items(), key=lambda kv: -sum(kv[1])):
+        timed = d[len(d) * warmup // (steps + warmup):]
+        lines.append("| `%s` | %d | %.1f |" % (k, len(timed), sum(timed) / len(timed)))
     with open(os.path.join(ROOT, "profiles", "kernel_trace_%s.md" % WORKLOAD), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -436,6 +455,19 @@ def main() -> int:
                   "gather_bytes": nb * (1 + 1.0 / 32), "gather_bytes_bf16": nb * 2.0,
                   "gather_ratio": round((1 + 1.0 / 32) / 2.0, 4)}
     del slab, so
+
+    # Achievable HBM rate for context: a plain device copy, alone with a clean
+    # cache, at the size of the 8192 x 4096 activation (64 MiB -> 64 MiB, the
+    # small quantizers' volume) and of the 28672 x 4096 weight (224 MiB).
+    hbm_copy = {}
+    for mib in (64, 224):
+        src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        t = alone(lambda: dst.copy_(src))
+        gbps = 2.0 * (mib << 20) / (t * 1e-3) / 1e9
+        hbm_copy["%dMiB" % mib] = {"ms": round(t, 4), "GBps": round(gbps, 1),
+                                   "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        del src, dst
     del flush
 
     if args.calibrate_copy:
@@ -485,6 +517,7 @@ def main() -> int:
         "quantize_GBps_isolated": round(quant_gbps_iso, 1),
         "fused_dual": fused_dual,
         "fsdp_shard": fsdp_shard,
+        "hbm_copy": hbm_copy,
         "quantize_frac_of_hbm_peak_isolated": round(quant_gbps_iso / PEAK_HBM_GBPS, 4),
         "kernels": [{kk: (round(v, 4) if isinstance(v, float) else
                           {a: round(b, 4) for a, b in v.items()} if isinstance(v, dict) else v)
@@ -505,6 +538,9 @@ def main() -> int:
         print("fsdp2 shard quantize (%s, e4m3): %.1f us alone, %.0f GB/s; gather payload %.3fx of bf16" % (
             fsdp_shard["slab"], fsdp_shard["ms"] * 1e3, fsdp_shard["GBps"], fsdp_shard["gather_ratio"]),
             file=sys.stderr)
+        for k, v in hbm_copy.items():
+            print("device copy %s -> %s: %.1f us alone, %.0f GB/s (%.1f%% of HBM peak)" % (
+                k, k, v["ms"] * 1e3, v["GBps"], 100 * v["frac_of_hbm_peak"]), file=sys.stderr)
     print(json.dumps(line), flush=True)
     return 0
 

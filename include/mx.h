@@ -130,6 +130,30 @@ mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t col
                                    void *stream);
 
 /*
+ * mx_quantize_transpose_sr -- mx_quantize_transpose (rotate = 0) or
+ * mx_hadamard32_quantize (rotate = 1, with sign_mask) with stochastic instead
+ * of nearest rounding of the elements; same scales, same layout.  Stochastic
+ * rounding is the randomised cast that the FP4-training article on hzrcw.cc
+ * (section 01) names as the common remedy for FP4 training, against which it
+ * argues for the deterministic rotation; it is here for that comparison.
+ * Each element q = y * 2^-e (y the block value after the optional rotation,
+ * e the block's scale exponent) lies between grid neighbours lo <= |q| < hi
+ * and rounds up iff its 32-bit random word r < floor(2^32 (|q|-lo)/(hi-lo)),
+ * so the up-probability is the fractional position to 32 bits; magnitudes
+ * at or above the largest normal saturate; signs are kept.  Random words:
+ * element t of output row c is element i = c * rows + t of the Philox4x32-10
+ * stream (Salmon, Moraes, Dror, Shaw, SC 2011): word i mod 4 of the block at
+ * counter (i / 4 low word, i / 4 high word, 0, 0) and key (seed low word,
+ * seed high word).  The result depends only on x and seed, not on the launch
+ * configuration.
+ *   rotate  0 or 1
+ * Sizes, layout, ownership and errors as mx_quantize_transpose.
+ */
+mx_status_t mx_quantize_transpose_sr(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, int rotate,
+                                     uint32_t sign_mask, uint64_t seed, mx_format_t fmt, void *codes, void *scales,
+                                     void *stream);
+
+/*
  * mx_quantize_dual -- the row form and the transposed form of x from one
  * read of x: codes_row / scales_row exactly as mx_quantize(x, fmt_row), and
  * codes_t / scales_t exactly as mx_quantize_transpose(x, fmt_t) (rotate = 0)

@@ -71,7 +71,7 @@ def lib() -> ctypes.CDLL:
             "oracle_hadamard32_quantize": [P, i64, i64, i64, u32, i32, P, P],
             "oracle_dequantize": [P, P, i64, i64, i32, P],
             "oracle_cast_sr_many": [P, P, P, i64, i32, P],
-            "oracle_sr_words": [ctypes.c_uint64, i64, P],
+            "oracle_sr_words": [ctypes.c_uint64, i64, i64, P],
             "oracle_quantize_transpose_sr": [P, i64, i64, i64, i32, u32, ctypes.c_uint64, i32, P, P],
         }.items():
             fn = getattr(L, name)
@@ -134,10 +134,10 @@ def philox4x32_10(ctr, key) -> np.ndarray:
     return out
 
 
-def sr_words(seed: int, n: int) -> np.ndarray:
-    """the random words of output elements 0 .. n-1 under `seed`"""
+def sr_words(seed: int, n: int, start: int = 0) -> np.ndarray:
+    """the random words of output elements start .. start+n-1 under `seed`"""
     out = np.empty(n, dtype=np.uint32)
-    _check(lib().oracle_sr_words(seed & (2**64 - 1), n, _ptr(out)))
+    _check(lib().oracle_sr_words(seed & (2**64 - 1), start, n, _ptr(out)))
     return out
 
 

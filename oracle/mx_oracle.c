@@ -296,11 +296,11 @@ int oracle_cast_sr_many(const double *v, const int32_t *e, const uint32_t *r, in
     return 0;
 }
 
-/* the random words the stochastic-rounding quantizer uses for elements 0 .. n-1 */
-int oracle_sr_words(uint64_t seed, int64_t n, uint32_t *out)
+/* the random words the stochastic-rounding quantizer uses for elements start .. start+n-1 */
+int oracle_sr_words(uint64_t seed, int64_t start, int64_t n, uint32_t *out)
 {
-    if (n < 0) return -1;
-    for (int64_t i = 0; i < n; i++) out[i] = sr_word((uint64_t)i, seed);
+    if (n < 0 || start < 0) return -1;
+    for (int64_t i = 0; i < n; i++) out[i] = sr_word((uint64_t)(start + i), seed);
     return 0;
 }
 

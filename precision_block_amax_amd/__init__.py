@@ -54,8 +54,10 @@ def lib() -> ctypes.CDLL:
         L.mx_quantize_transpose.argtypes = [P, i64, i64, i64, i32, P, P, P]
         L.mx_hadamard32_quantize.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
         L.mx_quantize_dual.argtypes = [P, i64, i64, i64, i32, P, P, i32, i32, u32, P, P, P]
+        L.mx_quantize_transpose_sr.argtypes = [P, i64, i64, i64, i32, u32, ctypes.c_uint64, i32, P, P, P]
         L.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
-        for fn in (L.mx_quantize, L.mx_quantize_transpose, L.mx_hadamard32_quantize, L.mx_gemm):
+        for fn in (L.mx_quantize, L.mx_quantize_transpose, L.mx_hadamard32_quantize, L.mx_quantize_dual,
+                   L.mx_quantize_transpose_sr, L.mx_gemm):
             fn.restype = ctypes.c_int
         L.mx_status_string.argtypes = [ctypes.c_int]
         L.mx_status_string.restype = ctypes.c_char_p
@@ -160,6 +162,20 @@ def hadamard32_quantize(x: torch.Tensor, fmt, sign_mask: int = 0, out=None,
     codes, scales = _outputs(x.device, cols, rows, f, out)
     _check(lib().mx_hadamard32_quantize(_ptr(x), rows, cols, _ldx(x), sign_mask & 0xFFFFFFFF, f,
                                         _ptr(codes), _ptr(scales), _stream(x.device, stream)))
+    return codes, scales
+
+
+def quantize_transpose_sr(x: torch.Tensor, fmt, seed: int, rotate: bool = False, sign_mask: int = 0, out=None,
+                          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mx_quantize_transpose_sr: quantize_transpose (or, with rotate, hadamard32_quantize) with
+    stochastic rounding driven by the Philox4x32-10 stream of `seed`"""
+    _check_bf16_2d(x)
+    f = _fmt(fmt)
+    rows, cols = x.shape
+    codes, scales = _outputs(x.device, cols, rows, f, out)
+    _check(lib().mx_quantize_transpose_sr(_ptr(x), rows, cols, _ldx(x), 1 if rotate else 0, sign_mask & 0xFFFFFFFF,
+                                          seed & (2 ** 64 - 1), f, _ptr(codes), _ptr(scales),
+                                          _stream(x.device, stream)))
     return codes, scales
 
 

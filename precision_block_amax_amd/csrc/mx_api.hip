@@ -110,6 +110,18 @@ mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t col
                                                   (hipStream_t)stream));
 }
 
+mx_status_t mx_quantize_transpose_sr(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, int rotate,
+                                     uint32_t sign_mask, uint64_t seed, mx_format_t fmt, void *codes, void *scales,
+                                     void *stream) {
+    if (rotate != 0 && rotate != 1) return MX_ERR_INVALID_ARG;
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt, codes, scales, true);
+    if (st != MX_OK || rows == 0 || cols == 0) return st;
+    if ((st = check_device()) != MX_OK) return st;
+    return launched(mx::launch_quantize_transpose_sr((const uint16_t *)x_bf16, rows, cols, ldx, fmt, rotate != 0,
+                                                     sign_mask, seed, (uint8_t *)codes, (uint8_t *)scales,
+                                                     (hipStream_t)stream));
+}
+
 mx_status_t mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt_row,
                              void *codes_row, void *scales_row, mx_format_t fmt_t, int rotate, uint32_t sign_mask,
                              void *codes_t, void *scales_t, void *stream) {

@@ -39,6 +39,11 @@ hipError_t launch_quantize_transpose(const uint16_t *x, int64_t rows, int64_t co
                                      int fmt, bool rotate, uint32_t sign_mask, uint8_t *codes,
                                      uint8_t *scales, hipStream_t stream);
 
+// transposed mode (rotated or not) with stochastic rounding under `seed`
+hipError_t launch_quantize_transpose_sr(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                        bool rotate, uint32_t sign_mask, uint64_t seed, uint8_t *codes,
+                                        uint8_t *scales, hipStream_t stream);
+
 // one read of x: row form (fmt_r) and transposed form (fmt_t, rotated or not)
 hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt_r,
                                 uint8_t *codes_r, uint8_t *scales_r, int fmt_t, bool rotate, uint32_t sign_mask,

@@ -65,7 +65,38 @@ hipError_t launch_tr_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t 
     return hipGetLastError();
 }
 
+template <int F, bool ROTATE>
+hipError_t launch_tr_sr_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint32_t mask, uint64_t seed,
+                            uint8_t *codes, uint8_t *scales, hipStream_t stream) {
+    const bool vec = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0) && ((uintptr_t)codes % 16 == 0);
+    const dim3 grid((unsigned)((cols + kTrCols - 1) / kTrCols), (unsigned)((rows / 32 + kTrBlocks - 1) / kTrBlocks));
+    if (vec)
+        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true, -1, true>), grid, dim3(64 * kTrWaves), 0, stream,
+                           x, ldx, rows, cols, mask, codes, scales, nullptr, nullptr, seed);
+    else
+        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, false, -1, true>), grid, dim3(64 * kTrWaves), 0, stream,
+                           x, ldx, rows, cols, mask, codes, scales, nullptr, nullptr, seed);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_quantize_transpose_sr(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                        bool rotate, uint32_t sign_mask, uint64_t seed, uint8_t *codes,
+                                        uint8_t *scales, hipStream_t stream) {
+    if (rotate) {
+        switch (fmt) {
+        case E4M3: return launch_tr_sr_fmt<E4M3, true>(x, rows, cols, ldx, sign_mask, seed, codes, scales, stream);
+        case E5M2: return launch_tr_sr_fmt<E5M2, true>(x, rows, cols, ldx, sign_mask, seed, codes, scales, stream);
+        default: return launch_tr_sr_fmt<E2M1, true>(x, rows, cols, ldx, sign_mask, seed, codes, scales, stream);
+        }
+    }
+    switch (fmt) {
+    case E4M3: return launch_tr_sr_fmt<E4M3, false>(x, rows, cols, ldx, 0, seed, codes, scales, stream);
+    case E5M2: return launch_tr_sr_fmt<E5M2, false>(x, rows, cols, ldx, 0, seed, codes, scales, stream);
+    default: return launch_tr_sr_fmt<E2M1, false>(x, rows, cols, ldx, 0, seed, codes, scales, stream);
+    }
+}
 
 hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                 uint8_t *codes, uint8_t *scales, hipStream_t stream) {

@@ -196,6 +196,60 @@ __device__ __forceinline__ void hadamard32(float (&y)[32], uint32_t sign_mask) {
     for (int i = 0; i < 32; i++) y[i] = __fmul_rn(y[i], c);
 }
 
+// ---------------------------------------------------------------------------
+// Stochastic rounding (the randomised cast the FP4-training article, section
+// 01, names as the common alternative to its deterministic scheme).  The rule:
+// with lo <= |q| < hi the neighbouring grid magnitudes, round up iff the
+// element's 32-bit random word r < floor(2^32 (|q| - lo) / (hi - lo));
+// saturate at the largest normal; keep the sign.  Random words come from
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): element i of the output takes word i mod 4 of the
+// block at counter (i / 4, 0, 0) under key (seed low, seed high).
+struct U4 { uint32_t x, y, z, w; };
+__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
+    uint32_t c2 = 0, c3 = 0;
+#pragma unroll
+    for (int round = 0; round < 10; round++) {
+        // multipliers and key increments of the published generator
+        const uint32_t h0 = __umulhi(0xD2511F53u, c0), l0 = 0xD2511F53u * c0;
+        const uint32_t h1 = __umulhi(0xCD9E8D57u, c2), l1 = 0xCD9E8D57u * c2;
+        const uint32_t n0 = h1 ^ c1 ^ k0, n2 = h0 ^ c3 ^ k1;
+        c0 = n0; c1 = l1; c2 = n2; c3 = l0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return U4{c0, c1, c2, c3};
+}
+
+// Grid parameters of the element formats: mantissa bits, exponent of the
+// smallest normal binade, largest normal.
+template <int F> struct Grid;
+template <> struct Grid<E4M3> { static constexpr int M = 3, EMIN = -6; static constexpr float MAX = 448.0f; };
+template <> struct Grid<E5M2> { static constexpr int M = 2, EMIN = -14; static constexpr float MAX = 57344.0f; };
+template <> struct Grid<E2M1> { static constexpr int M = 1, EMIN = 0; static constexpr float MAX = 6.0f; };
+
+// the grid value (unscaled, signed) that y * 2^-e rounds to under word r.
+// q = y * 2^-e is exact wherever it is an fp32 normal; below that every
+// format's spacing is so much larger that the up-probability truncates to 0
+// either way.  t = |q| / spacing, its integer and fractional parts and the
+// 32-bit fixed-point fraction are all exact in fp32.
+template <int F>
+__device__ __forceinline__ float sr_round(float y, int e, uint32_t r) {
+    const float q = __builtin_amdgcn_ldexpf(y, -e);
+    const float a = __builtin_fabsf(q);
+    float mag = Grid<F>::MAX;
+    if (a < Grid<F>::MAX) {
+        const int k = (int)(__float_as_uint(a) >> 23) - 127;   // -127 for zero and subnormals
+        const int kk = k < Grid<F>::EMIN ? Grid<F>::EMIN : k;  // binade whose spacing applies
+        const float t = __builtin_amdgcn_ldexpf(a, Grid<F>::M - kk);
+        float n = __builtin_floorf(t);
+        const uint32_t frac = (uint32_t)__builtin_amdgcn_ldexpf(t - n, 32);  // truncating conversion
+        n += r < frac ? 1.0f : 0.0f;
+        mag = __builtin_fminf(__builtin_amdgcn_ldexpf(n, kk - Grid<F>::M), Grid<F>::MAX);
+    }
+    return __builtin_copysignf(mag, q);
+}
+
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
@@ -210,11 +264,16 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 // each) and scales (8 bytes each) are collected in the wave's own LDS area
 // and written with 16-byte lanes: 4 or 8 store instructions per block
 // instead of 32 narrow ones, and one for the scales.
-template <int F, bool ROTATE, bool VEC, int FR = -1>
+//
+// SR selects stochastic rounding of the transposed form (no row form) with
+// the random words of `seed`; output element t of output row c is element
+// c * rows + t of the generator's stream.
+template <int F, bool ROTATE, bool VEC, int FR = -1, bool SR = false>
 __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
     const uint16_t *__restrict__ x, int64_t ldx, int64_t rows, int64_t cols, uint32_t sign_mask,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_r = nullptr,
-    uint8_t *__restrict__ scales_r = nullptr) {
+    uint8_t *__restrict__ scales_r = nullptr, uint64_t seed = 0) {
+    static_assert(!(SR && FR >= 0), "stochastic rounding is a transposed-form variant");
     constexpr int BB = F == E2M1 ? 16 : 32;             // code bytes per block of one output row
     constexpr int CB = kTrBlocks * BB;                  // staged bytes per output row: 128 or 256
     constexpr int NCH = CB / 16;                        // 16-byte chunks per output row
@@ -312,15 +371,31 @@ __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
             // bf16 inputs are exact in fp32, so the fp32 scale rule gives the bf16 one
             const bool finite = m < 0x7F800000u;
             const int e = scale_exp_f32<F>(finite ? m : 0u);
-            const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
+            float sc = __builtin_amdgcn_ldexpf(1.0f, e);
             const int c = cl + j;
+            if constexpr (SR) {
+                // replace y by its stochastically rounded grid values; the casts below then see
+                // representable values at scale 1 and are exact
+                const uint64_t base = ((uint64_t)(ctile + c) * (uint64_t)rows + (uint64_t)(rb * 32)) >> 2;
+                const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+                for (int g = 0; g < 8; g++) {
+                    const uint64_t ctr = base + g;
+                    const U4 r = philox4x32_10((uint32_t)ctr, (uint32_t)(ctr >> 32), k0, k1);
+                    y[4 * g + 0] = sr_round<F>(y[4 * g + 0], e, r.x);
+                    y[4 * g + 1] = sr_round<F>(y[4 * g + 1], e, r.y);
+                    y[4 * g + 2] = sr_round<F>(y[4 * g + 2], e, r.z);
+                    y[4 * g + 3] = sr_round<F>(y[4 * g + 3], e, r.w);
+                }
+                sc = 1.0f;
+            }
             if constexpr (F == E2M1) {
                 uint32_t q[4];
 #pragma unroll
                 for (int k = 0; k < 4; k++) q[k] = finite ? cvt8_fp4(y + 8 * k, sc) : 0u;
                 *reinterpret_cast<uint4 *>(&sC[c * CB + ((b ^ key(c)) << 4)]) = make_uint4(q[0], q[1], q[2], q[3]);
             } else {
-                const float lim = __builtin_amdgcn_ldexpf(MaxNormal<F>::v, e);
+                const float lim = SR ? MaxNormal<F>::v : __builtin_amdgcn_ldexpf(MaxNormal<F>::v, e);
                 uint32_t q[8];
 #pragma unroll
                 for (int k = 0; k < 8; k++) {

@@ -25,6 +25,7 @@ def L():
     lib.mx_quantize_transpose.argtypes = [P, i64, i64, i64, i32, P, P, P]
     lib.mx_hadamard32_quantize.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
     lib.mx_quantize_dual.argtypes = [P, i64, i64, i64, i32, P, P, i32, i32, u32, P, P, P]
+    lib.mx_quantize_transpose_sr.argtypes = [P, i64, i64, i64, i32, u32, ctypes.c_uint64, i32, P, P, P]
     lib.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
     lib.mx_status_string.argtypes = [ctypes.c_int]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -39,7 +40,7 @@ def declared_functions():
 def test_exports_every_declared_function(L):
     names = declared_functions()
     assert {"mx_quantize", "mx_quantize_transpose", "mx_hadamard32_quantize", "mx_quantize_dual",
-            "mx_gemm", "mx_status_string", "mx_version"} <= set(names)
+            "mx_quantize_transpose_sr", "mx_gemm", "mx_status_string", "mx_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), "libmx.so does not export %s" % n
 
@@ -78,6 +79,17 @@ def test_hadamard_rejects(L):
     assert f(X, 64, 4, 4, 0x9E3779B9, 5, C, S, None) == INVALID
     assert f(X, 64, 4, 3, 0, E2M1, C, S, None) == INVALID
     assert f(None, 0, 4, 4, 0, E2M1, None, None, None) == OK
+
+
+def test_sr_rejects(L):
+    f = L.mx_quantize_transpose_sr
+    assert f(X, 64, 4, 4, 2, 0, 1, E2M1, C, S, None) == INVALID             # rotate is 0 or 1
+    assert f(X, 33, 4, 4, 0, 0, 1, E2M1, C, S, None) == INVALID             # rows % 32
+    assert f(X, 64, 4, 4, 1, 0, 1, 5, C, S, None) == INVALID                # format
+    assert f(X, 64, 4, 3, 1, 0, 1, E2M1, C, S, None) == INVALID             # ldx < cols
+    assert f(X, 64, 4, 4, 1, 0, 1, E2M1, X, S, None) == INVALID             # codes overlap x
+    assert f(X, 64, 4, 4, 1, 0, 1, E2M1, None, S, None) == INVALID
+    assert f(None, 0, 4, 4, 1, 0, 1, E2M1, None, None, None) == OK          # empty
 
 
 def test_dual_rejects(L):

@@ -86,6 +86,10 @@ def test_sr_words_layout():
     key = [seed & 0xFFFFFFFF, seed >> 32]
     for blk in range(4):
         assert list(w[4 * blk:4 * blk + 4]) == list(oracle.philox4x32_10([blk, 0, 0, 0], key))
+    # the counter's high word carries i / 4 beyond 32 bits
+    i0 = (1 << 34) + 8
+    assert list(oracle.sr_words(seed, 4, start=i0)) == list(oracle.philox4x32_10([2, 1, 0, 0], key))
+    assert list(oracle.sr_words(seed, 6, start=5)) == list(w[5:11])
 
 
 @pytest.mark.parametrize("fmt", FMTS)
