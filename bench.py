@@ -289,8 +289,11 @@ def ablation(mx, torch, seed: int) -> dict:
     and X ~ N(0, 1), through the library's quantizers and GEMM, against the
     fp64 product of the same bf16 inputs.  Relative Frobenius error of:
     MXFP4 without rotation, with the fixed-sign rotation (two masks), with
-    random signs drawn anew for each of 8 steps, and MXFP8 without rotation.
-    Stochastic rounding is not built."""
+    random signs drawn anew for each of 8 steps, with stochastic rounding
+    (a new seed each step) with and without the fixed rotation, and MXFP8
+    without rotation.  For the randomised variants the error of the 8-step
+    average dW is given too: it falls below the single-step error only
+    where the steps' errors vary and cancel."""
     cfg = workloads.config(3)
     dy = workloads.draw_tensor(cfg, "dY", seed=seed)[:, :1024]
     x = workloads.draw_tensor(cfg, "X", seed=seed)[:, :512]
@@ -300,9 +303,20 @@ def ablation(mx, torch, seed: int) -> dict:
     dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to("cuda")
     dyd, xd = dev(dy), dev(x)
 
-    def dw(qa, qb, fmt):
+    def dw_mat(qa, qb, fmt):
         c = mx.gemm(qa[0], qa[1], fmt, qb[0], qb[1], fmt, out_dtype=torch.float32)
-        return float(np.linalg.norm(c.cpu().numpy().astype(np.float64) - ref) / nref)
+        return c.cpu().numpy().astype(np.float64)
+
+    def dw(qa, qb, fmt):
+        return float(np.linalg.norm(dw_mat(qa, qb, fmt) - ref) / nref)
+
+    def steps_of(make, n=8):
+        """relative error of each of n steps, and of their average dW (which
+        shrinks only where the steps' errors differ and cancel)"""
+        mats = [make(i) for i in range(n)]
+        errs = [float(np.linalg.norm(m - ref) / nref) for m in mats]
+        return {"mean": float(np.mean(errs)), "min": float(np.min(errs)), "max": float(np.max(errs)),
+                "error_of_the_%d_step_average" % n: float(np.linalg.norm(np.mean(mats, axis=0) - ref) / nref)}
 
     out = {"shape": "dW[1024x512] = dY[8192x1024]^T X[8192x512]", "metric": "||dW - dW_fp64||_F / ||dW_fp64||_F"}
     out["mxfp4_no_rotation"] = dw(mx.quantize_transpose(dyd, "e2m1"), mx.quantize_transpose(xd, "e2m1"), "e2m1")
@@ -316,6 +330,13 @@ def ablation(mx, torch, seed: int) -> dict:
         errs.append(dw(mx.hadamard32_quantize(dyd, "e2m1", mask), mx.hadamard32_quantize(xd, "e2m1", mask), "e2m1"))
     out["mxfp4_random_sign_rotation_8_steps"] = {"mean": float(np.mean(errs)), "min": float(np.min(errs)),
                                                  "max": float(np.max(errs))}
+    # stochastic rounding of both operands, a fresh seed per step (the two operands draw from
+    # disjoint parts of the stream through different seeds)
+    out["mxfp4_stochastic_rounding_8_steps"] = steps_of(lambda i: dw_mat(
+        mx.quantize_transpose_sr(dyd, "e2m1", 2 * i + 1), mx.quantize_transpose_sr(xd, "e2m1", 2 * i + 2), "e2m1"))
+    out["mxfp4_fixed_rotation_and_stochastic_rounding_8_steps"] = steps_of(lambda i: dw_mat(
+        mx.quantize_transpose_sr(dyd, "e2m1", 2 * i + 1, True, 0),
+        mx.quantize_transpose_sr(xd, "e2m1", 2 * i + 2, True, 0), "e2m1"))
     out["mxfp8_e4m3_no_rotation"] = dw(mx.quantize_transpose(dyd, "e4m3"), mx.quantize_transpose(xd, "e4m3"), "e4m3")
     return out
 
