@@ -92,11 +92,17 @@ __device__ __forceinline__ int swz(int row, int ch) {
     return row * RB + ((ch ^ swz_key<RB>(row)) << 4);
 }
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// fp32 -> bf16, round to nearest even, NaN kept as a quiet NaN.  The
+// gfx950 packed conversion (v_cvt_pk_bf16_f32, two values per instruction)
+// does exactly that: on the device it equals the integer rounding
+// (u + 0x7FFF + lsb) >> 16, with bit 6 set for NaN, on every one of the 2^32
+// fp32 patterns, NaN payloads included -- and costs one instruction per pair
+// instead of about six per value, which made the bf16 epilogue VALU-bound.
+typedef float v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{lo, hi}, v2bf));
 }
+__device__ __forceinline__ uint32_t bf16_rne(float f) { return bf16x2(f, 0.0f) & 0xFFFFu; }
 
 // XCD-aware tile order: wg -> (tile row, tile column)
 __device__ __forceinline__ void tile_of(const GemmArgs &g, int &m0, int &n0) {
@@ -526,7 +532,7 @@ __device__ __forceinline__ void barrier() {
 }
 
 // tile hand-over mark between the carrier's fast and exact kernels (see there)
-constexpr uint16_t kMarkBf16 = 0x7FBE;      // bf16 NaN, quiet bit clear: bf16_rne never yields it
+constexpr uint16_t kMarkBf16 = 0x7FBE;      // bf16 NaN, quiet bit clear: the conversion never yields it
 constexpr uint32_t kMarkF32 = 0x7FBADBADu;  // fp32 NaN, quiet bit clear: arithmetic never yields it
 template <bool BF16OUT>
 __device__ __forceinline__ void mark_tile(const GemmArgs &g, int m0, int n0) {
@@ -599,7 +605,7 @@ __device__ __forceinline__ void store_c4(const GemmArgs &g, int m, int n, float 
     if (m >= g.M) return;
     if (vec && n + 3 < g.N) {
         if constexpr (BF16OUT) {
-            const uint32_t lo = bf16_rne(v0) | (bf16_rne(v1) << 16), hi = bf16_rne(v2) | (bf16_rne(v3) << 16);
+            const uint32_t lo = bf16x2(v0, v1), hi = bf16x2(v2, v3);
             *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(g.c) + (int64_t)m * g.ldc + n) = make_uint2(lo, hi);
         } else {
             *reinterpret_cast<float4 *>(reinterpret_cast<float *>(g.c) + (int64_t)m * g.ldc + n) =
@@ -933,7 +939,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                             const int c = 4 * j + q;  // 8-byte half h of 16-byte chunk c
                             const int off = m * ROWB + ((c ^ (m & (CPR - 1))) << 4) + 8 * h;
                             *reinterpret_cast<uint2 *>(&reg[off]) =
-                                make_uint2(bf16_rne(v0) | (bf16_rne(v1) << 16), bf16_rne(v2) | (bf16_rne(v3) << 16));
+                                make_uint2(bf16x2(v0, v1), bf16x2(v2, v3));
                         } else {
                             const int c = 8 * j + 2 * q + h;
                             const int off = m * ROWB + ((c ^ (m & (CPR - 1))) << 4);
