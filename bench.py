@@ -477,6 +477,46 @@ def main() -> int:
                   "gather_ratio": round((1 + 1.0 / 32) / 2.0, 4)}
     del slab, so
 
+    # The full MXFP4 recipe and the mixed-format GEMMs at the gate/up layer's
+    # shapes, each alone with a clean cache: Dgrad in FP4 (dX = dY W through
+    # the transposed weight, K = 28672), FP8 activations x FP4 weights, the
+    # E5M2-gradient Dgrad of the MXFP8 recipe, and an FP4 GEMM whose M and N
+    # are not multiples of the 256 x 256 tile.  dY here is seeded Gaussian
+    # noise of scale 1e-3 drawn on the device (a timing input only).
+    gen = torch.Generator(device="cuda").manual_seed(args.seed)
+    dy = (torch.randn((8192, 28672), generator=gen, device="cuda") * 1e-3).to(torch.bfloat16)
+    xg = torch.from_numpy(workloads.draw_tensor(cfg2, "X", seed=args.seed).view(np.int16)).view(torch.bfloat16).to("cuda")
+    wg = torch.from_numpy(workloads.draw_tensor(cfg2, "W", seed=args.seed).view(np.int16)).view(torch.bfloat16).to("cuda")
+    recipe = {}
+
+    def rec(name, a, fa, b, fb, out_dtype, peak_key):
+        M, N, K = a[0].shape[0], b[0].shape[0], a[1].shape[1] * 32
+        c = torch.empty((M, N), dtype=out_dtype, device="cuda")
+        t = alone(lambda: mx.gemm(a[0], a[1], fa, b[0], b[1], fb, out_dtype=out_dtype, out=c))
+        tf = 2.0 * M * N * K / (t * 1e-3) / 1e12
+        r = {"M": M, "N": N, "K": K, "formats": "%sx%s" % (fa, fb), "ms": round(t, 4), "TFLOPs": round(tf, 1),
+             "peak": PEAK_TFLOPS[peak_key], "frac": round(tf / PEAK_TFLOPS[peak_key], 4)}
+        if peak_key == "bf16":
+            r["frac_of_mxfp8_peak"] = round(tf / PEAK_TFLOPS["fp8"], 4)
+        recipe[name] = r
+
+    q_dy4 = mx.quantize(dy, "e2m1")
+    q_wt4 = mx.quantize_transpose(wg, "e2m1")
+    rec("dgrad_fp4 dX = dY W", q_dy4, "e2m1", q_wt4, "e2m1", torch.bfloat16, "fp4")
+    del q_dy4
+    q_x8 = mx.quantize(xg, "e4m3")
+    q_w4 = mx.quantize(wg, "e2m1")
+    rec("fprop_e4m3_x_e2m1 Y = X W^T", q_x8, "e4m3", q_w4, "e2m1", torch.bfloat16, "bf16")
+    del q_x8
+    q_dy5 = mx.quantize(dy, "e5m2")
+    q_wt8 = mx.quantize_transpose(wg, "e4m3")
+    rec("dgrad_e5m2_x_e4m3 dX = dY W", q_dy5, "e5m2", q_wt8, "e4m3", torch.bfloat16, "bf16")
+    del q_dy5, q_wt8
+    q_x4 = mx.quantize(xg, "e2m1")
+    rec("fprop_fp4_tails 8000x28000", (q_x4[0][:8000], q_x4[1][:8000]), "e2m1",
+        (q_w4[0][:28000], q_w4[1][:28000]), "e2m1", torch.bfloat16, "fp4")
+    del q_x4, q_w4, q_wt4, dy, xg, wg
+
     # Achievable HBM rate for context: a plain device copy, alone with a clean
     # cache, at the size of the 8192 x 4096 activation (64 MiB -> 64 MiB, the
     # small quantizers' volume) and of the 28672 x 4096 weight (224 MiB).
@@ -539,6 +579,7 @@ def main() -> int:
         "fused_dual": fused_dual,
         "fsdp_shard": fsdp_shard,
         "hbm_copy": hbm_copy,
+        "mxfp4_recipe_and_mixed_gemms": recipe,
         "quantize_frac_of_hbm_peak_isolated": round(quant_gbps_iso / PEAK_HBM_GBPS, 4),
         "kernels": [{kk: (round(v, 4) if isinstance(v, float) else
                           {a: round(b, 4) for a, b in v.items()} if isinstance(v, dict) else v)
@@ -559,6 +600,10 @@ def main() -> int:
         print("fsdp2 shard quantize (%s, e4m3): %.1f us alone, %.0f GB/s; gather payload %.3fx of bf16" % (
             fsdp_shard["slab"], fsdp_shard["ms"] * 1e3, fsdp_shard["GBps"], fsdp_shard["gather_ratio"]),
             file=sys.stderr)
+        for k, v in recipe.items():
+            print("%-34s %5dx%5dx%5d %-10s %7.1f us alone, %6.0f TFLOP/s, %4.1f%% of %.0f" % (
+                k, v["M"], v["N"], v["K"], v["formats"], v["ms"] * 1e3, v["TFLOPs"], 100 * v["frac"], v["peak"]),
+                file=sys.stderr)
         for k, v in hbm_copy.items():
             print("device copy %s -> %s: %.1f us alone, %.0f GB/s (%.1f%% of HBM peak)" % (
                 k, k, v["ms"] * 1e3, v["GBps"], 100 * v["frac_of_hbm_peak"]), file=sys.stderr)
