@@ -6,7 +6,10 @@
 // quantized training (FP4-training article on hzrcw.cc, section 02), which
 // the Primus page identifies as the dominant training cost.
 //
-// Two kernels share one tiling (MFMA-bound; 2*M*N*K flops):
+// The main path is the pipelined kernel at the end of this file (namespace
+// pipe): 8 waves of 128 x 64, stage loads straight to LDS, used whenever K is
+// a multiple of 512 and the operands are aligned.  The general kernels below
+// cover every other shape; they share one tiling (MFMA-bound; 2*M*N*K flops):
 //   - workgroup tile 256 x 256, four waves of 128 x 128 (4 x 4 tiles of
 //     32 x 32, 256 fp32 accumulators per lane);
 //   - operand codes and scales double-buffered in LDS, the 16-byte chunks of
