@@ -49,7 +49,12 @@ PROFILE_COMMANDS = (
     "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write -- "
     "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
+    "rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/prof_clock -o clock -- "
+    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
 )
+XCDS = 8          # MI355X: GRBM_GUI_ACTIVE sums the busy cycles of the 8 accelerator dies
+PEAK_SCLK_GHZ = 2.4
+MIN_CLOCK_US = 100  # shortest kernel whose counted busy cycles give a clock
 
 
 def quant_bytes(rows: int, cols: int, fmt: str) -> float:
@@ -66,18 +71,29 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None"""
+def _profile_summary():
+    """the committed rocprofv3 counter summary, if it was taken on the current
+    kernel sources; else None"""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    if data.get("source_sha") != kernel_source_sha():
-        return None
-    k = data.get("kernels", {}).get(kernel)
+    return data if data.get("source_sha") == kernel_source_sha() else None
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None"""
+    data = _profile_summary()
+    k = None if data is None else data.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def measured_clock(kernel: str):
+    """sustained shader clock (GHz) of the kernel's timed step launches from the
+    committed counter summary, or None"""
+    data = _profile_summary()
+    return None if data is None else data.get("sclk_ghz", {}).get(kernel)
 
 
 class Step:
@@ -194,7 +210,7 @@ def _find(d, suffix):
     raise FileNotFoundError("%s/*%s" % (d, suffix))
 
 
-def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, command: str) -> None:
+def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir: str, command: str) -> None:
     """Turn rocprofv3 CSV output (kernel trace with stats; FETCH_SIZE and
     WRITE_SIZE counter passes with --calibrate-copy) into the short summaries
     kept under profiles/: per-kernel average durations, and HBM bytes per
@@ -276,9 +292,42 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, command: 
         lines.append("| `%s` | %.0f | %.0f | %.1f | %.1f |" % (k, f_kib[k], w_kib.get(k, 0.0), rd / 1e6, wr / 1e6))
     with open(os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % WORKLOAD), "w") as f:
         f.write("\n".join(lines) + "\n")
+    # sustained shader clock of each library kernel over its timed step launches (dispatches
+    # before the first cache-filling reduction, after the warm-up share): busy cycles summed over
+    # the dies / (dies x dispatch time)
+    rows = sorted(_read_csv(_find(clock_dir, "counter_collection.csv")), key=lambda r: int(r["Dispatch_Id"]))
+    first_flush_c = next((int(r["Dispatch_Id"]) for r in rows if "reduce" in r["Kernel_Name"].lower()), None)
+    csteps, cwarm = (int(a) for a in re.search(r"--steps (\d+) --warmup (\d+)", command[3]).groups())
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != "GRBM_GUI_ACTIVE" or "mx::" not in r["Kernel_Name"]:
+            continue
+        if first_flush_c is not None and int(r["Dispatch_Id"]) >= first_flush_c:
+            continue
+        dt = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if dt > 0:
+            per.setdefault(r["Kernel_Name"], []).append((float(r["Counter_Value"]) / (XCDS * dt), dt))
+    sclk = {}
+    lines = ["# Sustained shader clock per kernel (rocprofv3 GRBM_GUI_ACTIVE): %s" % WORKLOAD, "",
+             "Command (from the repository root on the GPU box):", "", "    " + command[3], "",
+             "GRBM_GUI_ACTIVE sums the busy cycles of the %d dies; clock = value / (%d x dispatch time), "
+             "averaged over the timed step launches (the last %d of every %d). The dense peaks assume "
+             "%.1f GHz. Kernels whose launches average under %d us are left out: their counts include "
+             "busy cycles outside the dispatch window (they read above the %.1f GHz maximum)." % (
+                 XCDS, XCDS, csteps, csteps + cwarm, PEAK_SCLK_GHZ, MIN_CLOCK_US, PEAK_SCLK_GHZ), "",
+             "| kernel | timed launches | average (us) | clock (GHz) |", "|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: kv[0]):
+        timed = v[len(v) * cwarm // (csteps + cwarm):]
+        us = sum(t for _, t in timed) / len(timed) / 1e3
+        if us < MIN_CLOCK_US:
+            continue
+        sclk[k] = sum(c for c, _ in timed) / len(timed)
+        lines.append("| `%s` | %d | %.1f | %.2f |" % (k, len(timed), us, sclk[k]))
+    with open(os.path.join(ROOT, "profiles", "sclk_%s.md" % WORKLOAD), "w") as f:
+        f.write("\n".join(lines) + "\n")
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump({"source_sha": kernel_source_sha(), "workload": WORKLOAD, "fetch_scale": f_scale,
-                   "write_scale": w_scale, "kernels": kern, "commands": command[1:]}, f, indent=1)
+                   "write_scale": w_scale, "kernels": kern, "sclk_ghz": sclk, "commands": command[1:]}, f, indent=1)
 
 
 # the kernel symbol each bench launch name runs (dominant kernel lookup in traffic.json)
@@ -363,7 +412,7 @@ def main() -> int:
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table to stderr")
     ap.add_argument("--ablation", action="store_true",
                     help="only the weight-gradient rotation ablation (dW error of the Wgrad recipes)")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+    ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "CLOCK_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 256 MiB device copy three times (HBM counter calibration)")
@@ -561,6 +610,10 @@ def main() -> int:
     traffic = measured_traffic(kernel_symbol(dom["kernel"]))
     roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3), "peak": dom["peak"],
                 "unit": dom["unit"], "frac": round(dom["frac"], 4), "traffic": traffic, "kernel": dom["kernel"]}
+    sclk = measured_clock(kernel_symbol(dom["kernel"]))
+    if sclk is not None:  # the profiled run's sustained clock: the peak the kernel could reach at it
+        roofline["sclk_ghz"] = round(sclk, 3)
+        roofline["frac_of_clock_adjusted_peak"] = round(dom["frac"] * PEAK_SCLK_GHZ / sclk, 4)
     q = [k for k in kernels if k["bound"] == "hbm"]
     quant_gbps = sum(k["work"] for k in q) / (sum(k["ms"] for k in q) * 1e-3) / 1e9
     quant_gbps_iso = sum(k["work"] for k in q) / (sum(k["isolated"]["ms"] for k in q) * 1e-3) / 1e9
