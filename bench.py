@@ -220,10 +220,17 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
     write = _read_csv(_find(write_dir, "counter_collection.csv"))
 
     def per_kernel(rows):
-        out = {}
+        # the step's own launches (before the first cache-filling reduction) where the kernel has
+        # any: the extra records after them run some kernels at other shapes
+        rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+        first = next((int(r["Dispatch_Id"]) for r in rows if "reduce" in r["Kernel_Name"].lower()), None)
+        step, rest = {}, {}
         for r in rows:
-            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in out.items()}
+            in_step = first is not None and int(r["Dispatch_Id"]) < first
+            (step if in_step else rest).setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        out = {k: sum(v) / len(v) for k, v in rest.items()}
+        out.update({k: sum(v) / len(v) for k, v in step.items()})
+        return out
 
     f_kib, w_kib = per_kernel(fetch), per_kernel(write)
     copy = [k for k in f_kib if "copyBuffer" in k or "copy" in k.lower()]
@@ -231,11 +238,15 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
         raise RuntimeError("no copy kernel in the counter passes (run bench.py with --calibrate-copy)")
 
     def largest_copy(rows):
-        # the 256 MiB calibration copy is the largest copy dispatch (torch also launches tiny copies)
+        # the 256 MiB calibration copies run last, after every library kernel (earlier copies
+        # include dtype conversions of other sizes)
+        last_mx = max(int(r["Dispatch_Id"]) for r in rows if "mx::" in r["Kernel_Name"])
         per = {}
         for r in rows:
-            if r["Kernel_Name"] in copy:
+            if r["Kernel_Name"] in copy and int(r["Dispatch_Id"]) > last_mx:
                 per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not per:
+            raise RuntimeError("no calibration copy after the library's kernels (run bench.py with --calibrate-copy)")
         return max(per.values())
 
     known_kib = 256 * 1024.0
@@ -281,8 +292,10 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
              "    " + command[1], "    " + command[2], "",
              "Calibration: a plain 256 MiB device copy (`%s`) reads FETCH_SIZE = %.0f KiB and "
              "WRITE_SIZE = %.0f KiB per dispatch for 262144 KiB read and written, so counter KiB are "
-             "scaled by %.4f (fetch) and %.4f (write). Kernels called at several sizes (the row "
-             "quantizers) show the mean over their calls." % (copy[0], f_copy, w_copy, f_scale, w_scale),
+             "scaled by %.4f (fetch) and %.4f (write). Each kernel's figure is the mean over its launches "
+             "inside the step (for a kernel the step runs at several sizes, such as the row quantizers, "
+             "the mean over those); kernels only the extra records run are averaged over their calls." % (
+                 copy[0], f_copy, w_copy, f_scale, w_scale),
              "", "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (MB) | written (MB) |", "|---|---|---|---|---|"]
     for k in f_kib:
         if k in copy or "mx::" not in k:
