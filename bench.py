@@ -210,7 +210,8 @@ def _find(d, suffix):
     raise FileNotFoundError("%s/*%s" % (d, suffix))
 
 
-def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir: str, command: str) -> None:
+def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir: str, command: str,
+                       out_dir: str = os.path.join(ROOT, "profiles")) -> None:
     """Turn rocprofv3 CSV output (kernel trace with stats; FETCH_SIZE and
     WRITE_SIZE counter passes with --calibrate-copy) into the short summaries
     kept under profiles/: per-kernel average durations, and HBM bytes per
@@ -252,7 +253,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
     known_kib = 256 * 1024.0
     f_copy, w_copy = largest_copy(fetch), largest_copy(write)
     f_scale, w_scale = known_kib / f_copy, known_kib / w_copy
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    os.makedirs(out_dir, exist_ok=True)
     lines = ["# rocprofv3 kernel trace: %s" % WORKLOAD, "",
              "Command (from the repository root on the GPU box):", "", "    " + command[0], "",
              "The library's kernels only (torch's kernels that fill the cache before each lone launch, "
@@ -283,7 +284,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
     for k, d in sorted(step_calls.items(), key=lambda kv: -sum(kv[1])):
         timed = d[len(d) * warmup // (steps + warmup):]
         lines.append("| `%s` | %d | %.1f |" % (k, len(timed), sum(timed) / len(timed)))
-    with open(os.path.join(ROOT, "profiles", "kernel_trace_%s.md" % WORKLOAD), "w") as f:
+    with open(os.path.join(out_dir, "kernel_trace_%s.md" % WORKLOAD), "w") as f:
         f.write("\n".join(lines) + "\n")
 
     kern = {}
@@ -303,7 +304,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
         rd, wr = f_kib[k] * f_scale * 1024, w_kib.get(k, 0.0) * w_scale * 1024
         kern[k] = {"read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr}
         lines.append("| `%s` | %.0f | %.0f | %.1f | %.1f |" % (k, f_kib[k], w_kib.get(k, 0.0), rd / 1e6, wr / 1e6))
-    with open(os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % WORKLOAD), "w") as f:
+    with open(os.path.join(out_dir, "hbm_traffic_%s.md" % WORKLOAD), "w") as f:
         f.write("\n".join(lines) + "\n")
     # sustained shader clock of each library kernel over its timed step launches (dispatches
     # before the first cache-filling reduction, after the warm-up share): busy cycles summed over
@@ -336,14 +337,13 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
             continue
         sclk[k] = sum(c for c, _ in timed) / len(timed)
         lines.append("| `%s` | %d | %.1f | %.2f |" % (k, len(timed), us, sclk[k]))
-    with open(os.path.join(ROOT, "profiles", "sclk_%s.md" % WORKLOAD), "w") as f:
+    with open(os.path.join(out_dir, "sclk_%s.md" % WORKLOAD), "w") as f:
         f.write("\n".join(lines) + "\n")
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
         json.dump({"source_sha": kernel_source_sha(), "workload": WORKLOAD, "fetch_scale": f_scale,
                    "write_scale": w_scale, "kernels": kern, "sclk_ghz": sclk, "commands": command[1:]}, f, indent=1)
 
 
-# the kernel symbol each bench launch name runs (dominant kernel lookup in traffic.json)
 def ablation(mx, torch, seed: int) -> dict:
     """Numerical proxy for the weight-gradient recipe (FP4-training article
     on hzrcw.cc, sections 02-03): dW = dY^T X over 8192 tokens with dY
@@ -404,7 +404,7 @@ def ablation(mx, torch, seed: int) -> dict:
 
 
 def kernel_symbol(name: str) -> str:
-    fa, fb = None, None
+    """the kernel symbol a bench launch name runs (GEMMs; other names are returned as they are)"""
     if "mx_gemm" in name:
         fa, fb = name.split()[-1].split("x")
         code = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
