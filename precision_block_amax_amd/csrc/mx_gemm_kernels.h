@@ -459,8 +459,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_carrier(GemmArgs g) {
                     const int sb = sBs[buf][(wn * 128 + j * 32 + l32) * SB + blk];
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
-                        const float v = __builtin_amdgcn_ldexpf(p[r], sa_r[r] + sb - 254);
-                        acc[i][j][r] += (sa_r[r] == 255 || sb == 255) ? __builtin_nanf("") : v;
+                        // an E8M0 NaN scale makes the term NaN (a select on the bit pattern)
+                        const uint32_t v = __float_as_uint(__builtin_amdgcn_ldexpf(p[r], sa_r[r] + sb - 254));
+                        acc[i][j][r] += __uint_as_float((sa_r[r] == 255 || sb == 255) ? 0x7FC00000u : v);
                     }
                 });
             });
@@ -868,8 +869,12 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                         const int sa = tSA[(wm * 128 + i * 32 + l32) * 16 + blk];
 #pragma unroll
                         for (int r = 0; r < 16; r++) {
-                            const float v = __builtin_amdgcn_ldexpf(p[r], sa + sb_r[r] - 254);
-                            acc[i][j][r] += (sa == 255 || sb_r[r] == 255) ? __builtin_nanf("") : v;
+                            // an E8M0 NaN scale makes the term NaN: a select on the bit pattern
+                            // (written as a conditional on floats, the compiler branched here and
+                            // spilled ~1800 registers around the branches)
+                            const uint32_t v = __float_as_uint(__builtin_amdgcn_ldexpf(p[r], sa + sb_r[r] - 254));
+                            const uint32_t nan_or_v = (sa == 255 || sb_r[r] == 255) ? 0x7FC00000u : v;
+                            acc[i][j][r] += __uint_as_float(nan_or_v);
                         }
                     });
                 });
