@@ -521,6 +521,21 @@ def main() -> int:
                   "separate_ms": round(t_row + t_rot, 4), "speedup": round((t_row + t_rot) / t_dual, 3)}
     del dy, outs, r_out, t_out
 
+    # The stochastic-rounding variant of the rotated gradient quantizer (the
+    # ablation's randomised cast; Philox words generated in the kernel) against
+    # the round-to-nearest kernel on the same gradient, each alone.
+    dy = torch.from_numpy(workloads.draw_tensor(cfg3, "dY", seed=args.seed).view(np.int16)).view(
+        torch.bfloat16).to("cuda")
+    sr_out = mx.quantize_transpose_sr(dy, "e2m1", 1, True, 0)
+    t_sr = alone(lambda: mx.quantize_transpose_sr(dy, "e2m1", 1, True, 0, out=sr_out))
+    t_rn = alone(lambda: mx.hadamard32_quantize(dy, "e2m1", 0, out=sr_out))
+    sr_bytes = quant_bytes(dy.shape[0], dy.shape[1], "e2m1")
+    stochastic_rounding = {"tensor": "%s/dY %dx%d" % (cfg3.name, dy.shape[0], dy.shape[1]),
+                           "format": "e2m1, rotated", "ms": round(t_sr, 4),
+                           "GBps": round(sr_bytes / (t_sr * 1e-3) / 1e9, 1),
+                           "nearest_rounding_ms": round(t_rn, 4), "slowdown": round(t_sr / t_rn, 3)}
+    del dy, sr_out
+
     # One rank's share of an FSDP2 MXFP8 weight all-gather: quantize its slab
     # of gate/up weight rows (1/8 of dim 0) to E4M3; the payload it
     # contributes to the gather is codes + scales instead of bf16.
@@ -644,6 +659,7 @@ def main() -> int:
         "quantize_GBps_isolated": round(quant_gbps_iso, 1),
         "fused_dual": fused_dual,
         "fsdp_shard": fsdp_shard,
+        "stochastic_rounding": stochastic_rounding,
         "hbm_copy": hbm_copy,
         "mxfp4_recipe_and_mixed_gemms": recipe,
         "quantize_frac_of_hbm_peak_isolated": round(quant_gbps_iso / PEAK_HBM_GBPS, 4),
@@ -666,6 +682,9 @@ def main() -> int:
         print("fsdp2 shard quantize (%s, e4m3): %.1f us alone, %.0f GB/s; gather payload %.3fx of bf16" % (
             fsdp_shard["slab"], fsdp_shard["ms"] * 1e3, fsdp_shard["GBps"], fsdp_shard["gather_ratio"]),
             file=sys.stderr)
+        print("stochastic-rounding quantize (%s, %s): %.1f us alone, %.0f GB/s; nearest rounding %.1f us" % (
+            stochastic_rounding["tensor"], stochastic_rounding["format"], stochastic_rounding["ms"] * 1e3,
+            stochastic_rounding["GBps"], stochastic_rounding["nearest_rounding_ms"] * 1e3), file=sys.stderr)
         for k, v in recipe.items():
             print("%-34s %5dx%5dx%5d %-10s %7.1f us alone, %6.0f TFLOP/s, %4.1f%% of %.0f" % (
                 k, v["M"], v["N"], v["K"], v["formats"], v["ms"] * 1e3, v["TFLOPs"], 100 * v["frac"], v["peak"]),
