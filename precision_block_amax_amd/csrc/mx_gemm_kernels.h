@@ -805,44 +805,78 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                 __builtin_amdgcn_sched_barrier(0);
             });
         } else if constexpr (MODE == 1) {
-            float sca[4][4], scb[2][4];
+            // Per row, the stage's four block exponents rebased on the row's reference:
+            // byte q = S_q - R + 127, which lies in [87, 127] for real blocks (scale spread
+            // <= 40 binades, S_q <= R), so 2^(S_q - R) <= 1 is the float with that byte
+            // as its exponent field.  Stages past the end of K and rows past the edge of
+            // the matrix hold zero codes and zero scale bytes, whose bytes wrap; the
+            // scale is clamped to 1 so that they stay finite and add exactly 0 (an
+            // exponent byte of 255 would be Inf, and 0 * Inf a NaN).
+            const auto rebase = [](uint32_t w, int R) -> uint32_t {
+                const uint32_t rr = __builtin_amdgcn_perm(0u, (uint32_t)R, 0u);  // R in every byte
+                return w - rr + 0x7F7F7F7Fu;  // bytewise S_q + 127 - R, no carries for real blocks
+            };
+            const auto block_scale = [](uint32_t d, int q) -> float {
+                const uint32_t b = ((d >> (8 * q)) & 0xFFu) << 23;
+                return __uint_as_float(b < 0x3F800000u ? b : 0x3F800000u);
+            };
+            uint32_t da[4], db[2];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int ra_ = wm * 128 + i * 32 + l32;
-                const uint32_t wa = *reinterpret_cast<const uint32_t *>(&tSA[ra_ * 16]);
-                const int Ra = sRa[ra_];
-#pragma unroll
-                for (int q = 0; q < 4; q++) sca[i][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wa >> (8 * q)) & 0xFF) - Ra);
+                da[i] = rebase(*reinterpret_cast<const uint32_t *>(&tSA[ra_ * 16]), sRa[ra_]);
             }
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 const int rb_ = wn * 64 + j * 32 + l32;
-                const uint32_t wb = *reinterpret_cast<const uint32_t *>(&tSB[rb_ * 16]);
-                const int Rb = sRb[rb_];
+                db[j] = rebase(*reinterpret_cast<const uint32_t *>(&tSB[rb_ * 16]), sRb[rb_]);
+            }
+            // Software-pipelined: step t + 1's codes are read from LDS at the top of step t
+            // and converted in the shadow of step t's MFMAs.  The MFMAs go column by
+            // column: the four on B fragment 0 first (they cover the LDS latency), then B
+            // fragment 0 of step t + 1 is converted into the registers they released, and
+            // each A fragment of step t + 1 right after the last MFMA that reads its
+            // predecessor, so about one step of fragments is live at a time.  (Converted
+            // just before their own MFMAs, with both waves of a SIMD released by the same
+            // barrier, the conversions and the matrix work had run one after the other.)
+            v8bf fa[4], fb[2];
 #pragma unroll
-                for (int q = 0; q < 4; q++) scb[j][q] = __builtin_amdgcn_ldexpf(1.0f, (int)((wb >> (8 * q)) & 0xFF) - Rb);
+            for (int i = 0; i < 4; i++) {
+                uint32_t lo, hi;
+                read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, 0, h, lo, hi);
+                fa[i] = to_bf16x8<FA>(lo, hi, block_scale(da[i], 0));
             }
 #pragma unroll
-            for (int t = 0; t < KE / 16; t++) {
-                v8bf fa[4], fb[2];
+            for (int j = 0; j < 2; j++) {
+                uint32_t lo, hi;
+                read_codes<FB, RBB>(tB, wn * 64 + j * 32 + l32, 0, h, lo, hi);
+                fb[j] = to_bf16x8<FB>(lo, hi, block_scale(db[j], 0));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, KE / 16>([&](auto step) {
+                constexpr int t = decltype(step)::value;
+                constexpr bool more = t + 1 < KE / 16;
+                uint32_t alo[4], ahi[4], blo[2], bhi[2];
+                if constexpr (more) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    uint32_t lo, hi;
-                    read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, t, h, lo, hi);
-                    fa[i] = to_bf16x8<FA>(lo, hi, sca[i][t >> 1]);
-                }
+                    for (int j = 0; j < 2; j++) read_codes<FB, RBB>(tB, wn * 64 + j * 32 + l32, t + 1, h, blo[j], bhi[j]);
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    uint32_t lo, hi;
-                    read_codes<FB, RBB>(tB, wn * 64 + j * 32 + l32, t, h, lo, hi);
-                    fb[j] = to_bf16x8<FB>(lo, hi, scb[j][t >> 1]);
+                    for (int i = 0; i < 4; i++) read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, t + 1, h, alo[i], ahi[i]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; i++)
-#pragma unroll
-                    for (int j = 0; j < 2; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-            }
+                    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0], fa[i], acc[i][0], 0, 0, 0);
+                if constexpr (more) fb[0] = to_bf16x8<FB>(blo[0], bhi[0], block_scale(db[0], (t + 1) >> 1));
+                __builtin_amdgcn_sched_barrier(0);
+                static_for<0, 4>([&](auto ii) {
+                    constexpr int i = decltype(ii)::value;
+                    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1], fa[i], acc[i][1], 0, 0, 0);
+                    if constexpr (more) fa[i] = to_bf16x8<FA>(alo[i], ahi[i], block_scale(da[i], (t + 1) >> 1));
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                if constexpr (more) fb[1] = to_bf16x8<FB>(blo[1], bhi[1], block_scale(db[1], (t + 1) >> 1));
+                __builtin_amdgcn_sched_barrier(0);
+            });
         } else {
 #pragma unroll 1
             for (int blk = 0; blk < KE / 32; blk++) {

@@ -177,6 +177,34 @@ def _random_codes(rng, rows, K, fmt):
     return c
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
+@pytest.mark.parametrize("K", [512, 1536, 2560])
+def test_carrier_zero_stages_reference_scales(mx, fa, fb, K):
+    """the FP8 carrier rebases each block's E8M0 byte on its row's largest one,
+    R; at these K its loop runs stages past the end of K, which hold zero codes
+    and zero scale bytes and must add exactly 0 for every R (with R = 128 a zero
+    byte once rebased to an Inf scale, and 0 * Inf put NaN across the row).
+    Rows' R cycle through 120..136; the other blocks lie up to 40 binades below."""
+    rng = np.random.default_rng(K + 7 * FMTS.index(fa) + FMTS.index(fb))
+    M, N = 256, 256
+    ca, cb = _random_codes(rng, M, K, fa), _random_codes(rng, N, K, fb)
+    kb = K // 32
+
+    def scales(rows, R):
+        s = (R[:, None] - rng.integers(0, 41, (rows, kb))).astype(np.uint8)
+        s[np.arange(rows), rng.integers(0, kb, rows)] = R  # each row reaches its R
+        return s
+
+    sa = scales(M, 120 + np.arange(M) % 17)
+    sb = scales(N, 120 + (3 * np.arange(N)) % 17)
+    assert (sa.max(axis=1) == 128).any() and (sb.max(axis=1) == 128).any()
+    C, S = oracle.gemm(ca, sa, fa, cb, sb, fb)
+    for bf16 in (False, True):
+        c = _host_c(_run(mx, (ca, sa), fa, (cb, sb), fb, bf16), bf16)
+        assert not np.isnan(c).any(), "NaN in C"
+        check_gemm(c, C, S, bf16)
+
+
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e2m1"), ("e2m1", "e5m2")])
 @pytest.mark.parametrize("spread", ["narrow", "full", "pathological"])
 def test_scale_spreads(mx, fa, fb, spread):
