@@ -802,6 +802,12 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                             v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0}, acc[i][j], 4, 4, sel,
                             (int)sbw[j][w], sel, (int)sa[i][w]);
                     }
+                // pin the order: left to itself the scheduler sank step s + 1's reads below
+                // six of step s's MFMAs, and step s + 1 then waited on their LDS latency
+                if constexpr (s + 1 < KE / 64) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // the six LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // then the eight MFMAs
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
         } else if constexpr (MODE == 1) {
