@@ -757,8 +757,11 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    // stage held in code buffer S whose scales are bytes SBY * P .. of slot T
-    auto compute = [&](auto S, auto T, auto P) {
+    // stage held in code buffer S whose scales are bytes SBY * P .. of slot T;
+    // issue_next() sends the next stage's loads (to the other buffer) once this
+    // stage's first LDS reads are out, so that their issue overlaps the reads'
+    // latency instead of delaying them
+    auto compute = [&](auto S, auto T, auto P, auto &&issue_next) {
         const uint8_t *tA = stA(S), *tB = stB(S);
         const uint8_t *tSA = stS(T, 0) + SBY * decltype(P)::value, *tSB = stS(T, 1) + SBY * decltype(P)::value;
         if constexpr (MODE == 0) {
@@ -788,6 +791,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                     fb[b][j] = *reinterpret_cast<const uint4 *>(&tB[swz<RBB>(wn * 64 + j * 32 + l32, 2 * s + h)]);
             };
             load(std::integral_constant<int, 0>{});
+            issue_next();
             static_for<0, KE / 64>([&](auto step) {
                 constexpr int s = decltype(step)::value, b = s & 1;
                 constexpr int w = s / 2, sel = (2 * s) % 4;
@@ -846,17 +850,17 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
             // just before their own MFMAs, with both waves of a SIMD released by the same
             // barrier, the conversions and the matrix work had run one after the other.)
             v8bf fa[4], fb[2];
+            {
+                uint32_t alo[4], ahi[4], blo[2], bhi[2];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                uint32_t lo, hi;
-                read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, 0, h, lo, hi);
-                fa[i] = to_bf16x8<FA>(lo, hi, block_scale(da[i], 0));
-            }
+                for (int i = 0; i < 4; i++) read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, 0, h, alo[i], ahi[i]);
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                uint32_t lo, hi;
-                read_codes<FB, RBB>(tB, wn * 64 + j * 32 + l32, 0, h, lo, hi);
-                fb[j] = to_bf16x8<FB>(lo, hi, block_scale(db[j], 0));
+                for (int j = 0; j < 2; j++) read_codes<FB, RBB>(tB, wn * 64 + j * 32 + l32, 0, h, blo[j], bhi[j]);
+                issue_next();
+#pragma unroll
+                for (int i = 0; i < 4; i++) fa[i] = to_bf16x8<FA>(alo[i], ahi[i], block_scale(da[i], 0));
+#pragma unroll
+                for (int j = 0; j < 2; j++) fb[j] = to_bf16x8<FB>(blo[j], bhi[j], block_scale(db[j], 0));
             }
             __builtin_amdgcn_sched_barrier(0);
             static_for<0, KE / 16>([&](auto step) {
@@ -884,6 +888,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                 __builtin_amdgcn_sched_barrier(0);
             });
         } else {
+            issue_next();
 #pragma unroll 1
             for (int blk = 0; blk < KE / 32; blk++) {
                 static_for<0, 2>([&](auto jj) {
@@ -935,14 +940,16 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
             const int kt = kt0 + u;  // stage computed in this step
             wait_vm<0>();  // this stage's loads
             barrier();
-            issue(std::integral_constant<int, (u + 1) % 2>{}, std::integral_constant<int, ((u + 1) / SPS) % 2>{},
-                  std::integral_constant<bool, (u + 1) % SPS == 0>{}, kt + 1);
             // unconditional: a stage past the end holds zero codes and zero
             // scale bytes (out-of-range loads), which add exactly 0; a branch
             // here would let the compiler sink the stage's MFMAs past the next
             // barrier and keep every fragment of the stage live across it
             compute(std::integral_constant<int, u % 2>{}, std::integral_constant<int, u / SPS>{},
-                    std::integral_constant<int, u % SPS>{});
+                    std::integral_constant<int, u % SPS>{}, [&] {
+                        issue(std::integral_constant<int, (u + 1) % 2>{},
+                              std::integral_constant<int, ((u + 1) / SPS) % 2>{},
+                              std::integral_constant<bool, (u + 1) % SPS == 0>{}, kt + 1);
+                    });
         });
     }
     wait_vm<0>();  // drain the out-of-range stage loads before the workgroup ends
