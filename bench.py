@@ -119,14 +119,27 @@ class Step:
                 codes = torch.empty((out_rows, mx.code_cols(k, q.fmt)), dtype=torch.uint8, device=dev)
                 scales = torch.empty((out_rows, k // 32), dtype=torch.uint8, device=dev)
                 ops[q.name] = (codes, scales, q.fmt)
-                fn = {"row": lambda x=x, q=q, c=codes, s=scales: mx.quantize(x, q.fmt, out=(c, s)),
-                      "transpose": lambda x=x, q=q, c=codes, s=scales: mx.quantize_transpose(x, q.fmt, out=(c, s)),
-                      "hadamard": lambda x=x, q=q, c=codes, s=scales: mx.hadamard32_quantize(
-                          x, q.fmt, q.sign_mask, out=(c, s))}[q.kind]
-                kname = {"row": "mx_quantize", "transpose": "mx_quantize_transpose",
-                         "hadamard": "mx_hadamard32_quantize"}[q.kind]
-                self.launches.append(("%s/%s %s %s" % (cfg.name, q.name, kname, q.fmt), "quant",
-                                      quant_bytes(rows, cols, q.fmt), fn))
+            qs = cfg.quants
+            if len(qs) == 2 and len({(q.kind, q.fmt, q.sign_mask) for q in qs}) == 1:
+                # both operands of the GEMM in one launch (mx_quantize_pair)
+                q0, q1 = qs
+                x0, x1 = tens[q0.tensor], tens[q1.tensor]
+                fn = (lambda q0=q0, x0=x0, x1=x1, o0=ops[q0.name][:2], o1=ops[q1.name][:2]: mx.quantize_pair(
+                    q0.kind, x0, x1, q0.fmt, q0.sign_mask, out0=o0, out1=o1))
+                self.launches.append(("%s/%s+%s mx_quantize_pair %s %s" % (cfg.name, q0.name, q1.name, q0.kind, q0.fmt),
+                                      "quant", quant_bytes(*x0.shape, q0.fmt) + quant_bytes(*x1.shape, q1.fmt), fn))
+            else:
+                for q in qs:
+                    x = tens[q.tensor]
+                    codes, scales = ops[q.name][:2]
+                    fn = {"row": lambda x=x, q=q, c=codes, s=scales: mx.quantize(x, q.fmt, out=(c, s)),
+                          "transpose": lambda x=x, q=q, c=codes, s=scales: mx.quantize_transpose(x, q.fmt, out=(c, s)),
+                          "hadamard": lambda x=x, q=q, c=codes, s=scales: mx.hadamard32_quantize(
+                              x, q.fmt, q.sign_mask, out=(c, s))}[q.kind]
+                    kname = {"row": "mx_quantize", "transpose": "mx_quantize_transpose",
+                             "hadamard": "mx_hadamard32_quantize"}[q.kind]
+                    self.launches.append(("%s/%s %s %s" % (cfg.name, q.name, kname, q.fmt), "quant",
+                                          quant_bytes(*x.shape, q.fmt), fn))
             for gm in cfg.gemms:
                 a, b = ops[gm.a], ops[gm.b]
                 out = torch.empty((gm.M, gm.N), dtype=torch.bfloat16 if gm.out == "bf16" else torch.float32,

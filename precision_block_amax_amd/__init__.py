@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "E4M3", "E5M2", "E2M1", "MXError", "lib", "library_path", "code_cols",
-    "quantize", "quantize_transpose", "hadamard32_quantize", "gemm",
+    "quantize", "quantize_transpose", "hadamard32_quantize", "quantize_pair", "gemm",
 ]
 
 E4M3, E5M2, E2M1 = 0, 1, 2
@@ -55,9 +55,10 @@ def lib() -> ctypes.CDLL:
         L.mx_hadamard32_quantize.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
         L.mx_quantize_dual.argtypes = [P, i64, i64, i64, i32, P, P, i32, i32, u32, P, P, P]
         L.mx_quantize_transpose_sr.argtypes = [P, i64, i64, i64, i32, u32, ctypes.c_uint64, i32, P, P, P]
+        L.mx_quantize_pair.argtypes = [i32, i32, u32, P, i64, i64, i64, P, P, P, i64, i64, i64, P, P, P]
         L.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
         for fn in (L.mx_quantize, L.mx_quantize_transpose, L.mx_hadamard32_quantize, L.mx_quantize_dual,
-                   L.mx_quantize_transpose_sr, L.mx_gemm):
+                   L.mx_quantize_transpose_sr, L.mx_quantize_pair, L.mx_gemm):
             fn.restype = ctypes.c_int
         L.mx_status_string.argtypes = [ctypes.c_int]
         L.mx_status_string.restype = ctypes.c_char_p
@@ -177,6 +178,33 @@ def quantize_transpose_sr(x: torch.Tensor, fmt, seed: int, rotate: bool = False,
                                           seed & (2 ** 64 - 1), f, _ptr(codes), _ptr(scales),
                                           _stream(x.device, stream)))
     return codes, scales
+
+
+_PAIR_MODES = {"row": 0, "transpose": 1, "hadamard": 2}
+
+
+def quantize_pair(mode: str, x0: torch.Tensor, x1: torch.Tensor, fmt, sign_mask: int = 0, out0=None, out1=None,
+                  stream=None):
+    """mx_quantize_pair: both operands of a GEMM in one launch, each exactly as quantize
+    (mode "row"), quantize_transpose ("transpose") or hadamard32_quantize ("hadamard", with
+    sign_mask) would quantize it.  Returns ((codes0, scales0), (codes1, scales1))."""
+    if mode not in _PAIR_MODES:
+        raise ValueError("mode must be one of %s" % sorted(_PAIR_MODES))
+    _check_bf16_2d(x0)
+    _check_bf16_2d(x1)
+    if x0.device != x1.device:
+        raise ValueError("both tensors must be on the same device")
+    f = _fmt(fmt)
+    outs = []
+    for x, out in ((x0, out0), (x1, out1)):
+        rows, cols = x.shape
+        outs.append(_outputs(x.device, rows, cols, f, out) if mode == "row" else _outputs(x.device, cols, rows, f, out))
+    (c0, s0), (c1, s1) = outs
+    _check(lib().mx_quantize_pair(_PAIR_MODES[mode], f, sign_mask & 0xFFFFFFFF,
+                                  _ptr(x0), x0.shape[0], x0.shape[1], _ldx(x0), _ptr(c0), _ptr(s0),
+                                  _ptr(x1), x1.shape[0], x1.shape[1], _ldx(x1), _ptr(c1), _ptr(s1),
+                                  _stream(x0.device, stream)))
+    return (c0, s0), (c1, s1)
 
 
 def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, fa, b_codes: torch.Tensor,

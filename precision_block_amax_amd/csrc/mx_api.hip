@@ -141,6 +141,39 @@ mx_status_t mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int
                                              (uint8_t *)scales_t, (hipStream_t)stream));
 }
 
+mx_status_t mx_quantize_pair(mx_pair_mode_t mode, mx_format_t fmt, uint32_t sign_mask, const void *x0,
+                             int64_t rows0, int64_t cols0, int64_t ldx0, void *codes0, void *scales0, const void *x1,
+                             int64_t rows1, int64_t cols1, int64_t ldx1, void *codes1, void *scales1, void *stream) {
+    if (mode != MX_PAIR_ROW && mode != MX_PAIR_TRANSPOSE && mode != MX_PAIR_HADAMARD) return MX_ERR_INVALID_ARG;
+    const bool tr = mode != MX_PAIR_ROW;
+    mx_status_t st = check_quant(x0, rows0, cols0, ldx0, fmt, codes0, scales0, tr);
+    if (st != MX_OK) return st;
+    if ((st = check_quant(x1, rows1, cols1, ldx1, fmt, codes1, scales1, tr)) != MX_OK) return st;
+    const bool e0 = rows0 == 0 || cols0 == 0, e1 = rows1 == 0 || cols1 == 0;
+    if (e0 && e1) return MX_OK;
+    if (!e0 && !e1) {
+        // no output of one tensor may overlap the other tensor's input or outputs
+        const int64_t n0 = rows0 * cols0, n1 = rows1 * cols1;
+        const int64_t xb0 = ((rows0 - 1) * ldx0 + cols0) * 2, xb1 = ((rows1 - 1) * ldx1 + cols1) * 2;
+        const int64_t cb0 = code_bytes(n0, fmt), cb1 = code_bytes(n1, fmt), sb0 = n0 / 32, sb1 = n1 / 32;
+        if (overlap(codes0, cb0, x1, xb1) || overlap(codes0, cb0, codes1, cb1) || overlap(codes0, cb0, scales1, sb1) ||
+            overlap(scales0, sb0, x1, xb1) || overlap(scales0, sb0, codes1, cb1) || overlap(scales0, sb0, scales1, sb1) ||
+            overlap(codes1, cb1, x0, xb0) || overlap(scales1, sb1, x0, xb0))
+            return MX_ERR_INVALID_ARG;
+    }
+    if ((st = check_device()) != MX_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    const mx::QuantJob j0{(const uint16_t *)x0, rows0, cols0, ldx0, (uint8_t *)codes0, (uint8_t *)scales0};
+    const mx::QuantJob j1{(const uint16_t *)x1, rows1, cols1, ldx1, (uint8_t *)codes1, (uint8_t *)scales1};
+    if (e0 || e1) {  // one tensor: the single call
+        const mx::QuantJob &j = e0 ? j1 : j0;
+        if (!tr) return launched(mx::launch_quantize_rows(j.x, j.rows, j.cols, j.ldx, fmt, j.codes, j.scales, s));
+        return launched(mx::launch_quantize_transpose(j.x, j.rows, j.cols, j.ldx, fmt, mode == MX_PAIR_HADAMARD,
+                                                      sign_mask, j.codes, j.scales, s));
+    }
+    return launched(mx::launch_quantize_pair((int)mode, fmt, mode == MX_PAIR_HADAMARD ? sign_mask : 0u, j0, j1, s));
+}
+
 mx_status_t mx_gemm(const void *a_codes, const void *a_scales, mx_format_t fa, const void *b_codes,
                     const void *b_scales, mx_format_t fb, int64_t M, int64_t N, int64_t K, void *c,
                     mx_out_t out, int64_t ldc, void *stream) {

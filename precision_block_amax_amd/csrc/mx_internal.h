@@ -15,7 +15,7 @@ namespace mx {
 // 32-bit n (the add is done in 64 bits).
 struct FastDiv {
     uint32_t d, m, l;
-    FastDiv() : d(1), m(1), l(0) {}
+    MXHD FastDiv() : d(1), m(1), l(0) {}
     explicit FastDiv(uint32_t div) : d(div) {
         l = 0;
         while ((1ull << l) < div) l++;
@@ -48,6 +48,18 @@ hipError_t launch_quantize_transpose_sr(const uint16_t *x, int64_t rows, int64_t
 hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt_r,
                                 uint8_t *codes_r, uint8_t *scales_r, int fmt_t, bool rotate, uint32_t sign_mask,
                                 uint8_t *codes_t, uint8_t *scales_t, hipStream_t stream);
+
+// one tensor of a pair quantization: bf16 input [rows x ldx], outputs as the single call's
+struct QuantJob {
+    const uint16_t *x;
+    int64_t rows, cols, ldx;
+    uint8_t *codes, *scales;
+};
+
+// Both tensors in one launch (mode 0: row, 1: transposed, 2: rotated transposed), or
+// two launches where they need different kernel variants.  Both non-empty.
+hipError_t launch_quantize_pair(int mode, int fmt, uint32_t sign_mask, const QuantJob &a, const QuantJob &b,
+                                hipStream_t stream);
 
 // GEMM launcher (mx_gemm.hip).
 hipError_t launch_gemm(const uint8_t *a, const uint8_t *as, int fa, const uint8_t *b,

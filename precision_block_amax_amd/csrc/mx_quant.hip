@@ -79,6 +79,50 @@ hipError_t launch_tr_sr_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64
     return hipGetLastError();
 }
 
+// Both operands of a GEMM in one launch (see mx_quantize_pair): the second
+// tensor's workgroups follow the first's.  Tensors that need different
+// kernel variants (row strides, alignment) take two launches instead.
+template <int F>
+hipError_t launch_rows_pair_fmt(const QuantJob &a, const QuantJob &b, hipStream_t stream) {
+    const uint32_t per_block = kRowThreads * kRowUnroll;
+    auto flags = [](const QuantJob &j, bool &contig, bool &vec) {
+        contig = j.ldx == j.cols;
+        vec = ((uintptr_t)j.x % 16 == 0) && (j.ldx % 8 == 0) && ((uintptr_t)j.codes % (F == E2M1 ? 4 : 8) == 0);
+    };
+    bool ca, va, cb, vb;
+    flags(a, ca, va);
+    flags(b, cb, vb);
+    const uint64_t ta = (uint64_t)a.rows * (uint64_t)a.cols / 8, tb = (uint64_t)b.rows * (uint64_t)b.cols / 8;
+    const uint64_t ga = (ta + per_block - 1) / per_block, gb = (tb + per_block - 1) / per_block;
+    if (!(ca && va && cb && vb) || ga + gb >= ((uint64_t)1 << 31)) {
+        const hipError_t e = launch_rows_fmt<F>(a.x, a.rows, a.cols, a.ldx, a.codes, a.scales, stream);
+        return e != hipSuccess ? e : launch_rows_fmt<F>(b.x, b.rows, b.cols, b.ldx, b.codes, b.scales, stream);
+    }
+    const FastDiv da((uint32_t)(a.cols / 8)), db((uint32_t)(b.cols / 8));
+    hipLaunchKernelGGL((k_quantize_rows<F, true, true, true>), dim3((unsigned)(ga + gb)), dim3(kRowThreads), 0, stream,
+                       a.x, a.ldx, (uint32_t)ta, (uint32_t)(a.cols / 8), da, a.codes, a.scales,
+                       b.x, b.ldx, (uint32_t)tb, (uint32_t)(b.cols / 8), db, b.codes, b.scales, (uint32_t)ga);
+    return hipGetLastError();
+}
+
+template <int F, bool ROTATE>
+hipError_t launch_tr_pair_fmt(const QuantJob &a, const QuantJob &b, uint32_t mask, hipStream_t stream) {
+    auto vec = [](const QuantJob &j) {
+        return ((uintptr_t)j.x % 8 == 0) && (j.ldx % 4 == 0) && ((uintptr_t)j.codes % 16 == 0);
+    };
+    if (!vec(a) || !vec(b)) {
+        const hipError_t e = launch_tr_fmt<F, ROTATE>(a.x, a.rows, a.cols, a.ldx, mask, a.codes, a.scales, stream);
+        return e != hipSuccess ? e : launch_tr_fmt<F, ROTATE>(b.x, b.rows, b.cols, b.ldx, mask, b.codes, b.scales, stream);
+    }
+    const uint32_t tx = (uint32_t)((a.cols + kTrCols - 1) / kTrCols), ux = (uint32_t)((b.cols + kTrCols - 1) / kTrCols);
+    const int64_t ra = (a.rows / 32 + kTrBlocks - 1) / kTrBlocks, rb = (b.rows / 32 + kTrBlocks - 1) / kTrBlocks;
+    const dim3 grid(tx + ux, (unsigned)(ra > rb ? ra : rb));
+    hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true, -1, false, true>), grid, dim3(64 * kTrWaves), 0, stream,
+                       a.x, a.ldx, a.rows, a.cols, mask, a.codes, a.scales, nullptr, nullptr, (uint64_t)0,
+                       b.x, b.ldx, b.rows, b.cols, b.codes, b.scales, tx);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize_transpose_sr(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
@@ -121,6 +165,29 @@ hipError_t launch_quantize_transpose(const uint16_t *x, int64_t rows, int64_t co
     case E4M3: return launch_tr_fmt<E4M3, false>(x, rows, cols, ldx, 0, codes, scales, stream);
     case E5M2: return launch_tr_fmt<E5M2, false>(x, rows, cols, ldx, 0, codes, scales, stream);
     default: return launch_tr_fmt<E2M1, false>(x, rows, cols, ldx, 0, codes, scales, stream);
+    }
+}
+
+hipError_t launch_quantize_pair(int mode, int fmt, uint32_t sign_mask, const QuantJob &a, const QuantJob &b,
+                                hipStream_t stream) {
+    if (mode == 0) {
+        switch (fmt) {
+        case E4M3: return launch_rows_pair_fmt<E4M3>(a, b, stream);
+        case E5M2: return launch_rows_pair_fmt<E5M2>(a, b, stream);
+        default: return launch_rows_pair_fmt<E2M1>(a, b, stream);
+        }
+    }
+    if (mode == 2) {
+        switch (fmt) {
+        case E4M3: return launch_tr_pair_fmt<E4M3, true>(a, b, sign_mask, stream);
+        case E5M2: return launch_tr_pair_fmt<E5M2, true>(a, b, sign_mask, stream);
+        default: return launch_tr_pair_fmt<E2M1, true>(a, b, sign_mask, stream);
+        }
+    }
+    switch (fmt) {
+    case E4M3: return launch_tr_pair_fmt<E4M3, false>(a, b, 0, stream);
+    case E5M2: return launch_tr_pair_fmt<E5M2, false>(a, b, 0, stream);
+    default: return launch_tr_pair_fmt<E2M1, false>(a, b, 0, stream);
     }
 }
 

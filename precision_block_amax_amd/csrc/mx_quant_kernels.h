@@ -86,12 +86,23 @@ __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d 
 
 // ---------------------------------------------------------------------------
 // Row mode.  Octet o covers elements 8o .. 8o+7 of the row-major [rows x cols]
-// view; cols % 32 == 0 keeps every block inside one quad of lanes.
-template <int F, bool CONTIG, bool VEC>
+// view; cols % 32 == 0 keeps every block inside one quad of lanes.  With
+// PAIR, workgroups from `split` on quantize a second tensor (x1 ...), so that
+// both operands of a GEMM take one launch.
+template <int F, bool CONTIG, bool VEC, bool PAIR = false>
 __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
     const uint16_t *__restrict__ x, int64_t ldx, uint32_t total_oct, uint32_t oct_per_row,
-    FastDiv row_div, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
-    const uint32_t o0 = blockIdx.x * (kRowThreads * kRowUnroll) + threadIdx.x;
+    FastDiv row_div, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+    const uint16_t *__restrict__ x1 = nullptr, int64_t ldx1 = 0, uint32_t total_oct1 = 0,
+    uint32_t oct_per_row1 = 0, FastDiv row_div1 = FastDiv(), uint8_t *__restrict__ codes1 = nullptr,
+    uint8_t *__restrict__ scales1 = nullptr, uint32_t split = 0) {
+    uint32_t blk = blockIdx.x;
+    if (PAIR && blk >= split) {  // uniform across the workgroup
+        blk -= split;
+        x = x1; ldx = ldx1; total_oct = total_oct1; oct_per_row = oct_per_row1; row_div = row_div1;
+        codes = codes1; scales = scales1;
+    }
+    const uint32_t o0 = blk * (kRowThreads * kRowUnroll) + threadIdx.x;
     uint32_t w[kRowUnroll][4];
 
 #pragma unroll
@@ -272,12 +283,25 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 // SR selects stochastic rounding of the transposed form (no row form) with
 // the random words of `seed`; output element t of output row c is element
 // c * rows + t of the generator's stream.
-template <int F, bool ROTATE, bool VEC, int FR = -1, bool SR = false>
+//
+// PAIR: workgroup columns from `split` on quantize a second tensor (x1 ...),
+// so that both operands of a GEMM take one launch; the grid's rows cover the
+// taller of the two, and a workgroup past its tensor's last row block writes
+// nothing.
+template <int F, bool ROTATE, bool VEC, int FR = -1, bool SR = false, bool PAIR = false>
 __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
     const uint16_t *__restrict__ x, int64_t ldx, int64_t rows, int64_t cols, uint32_t sign_mask,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_r = nullptr,
-    uint8_t *__restrict__ scales_r = nullptr, uint64_t seed = 0) {
+    uint8_t *__restrict__ scales_r = nullptr, uint64_t seed = 0, const uint16_t *__restrict__ x1 = nullptr,
+    int64_t ldx1 = 0, int64_t rows1 = 0, int64_t cols1 = 0, uint8_t *__restrict__ codes1 = nullptr,
+    uint8_t *__restrict__ scales1 = nullptr, uint32_t split = 0) {
     static_assert(!(SR && FR >= 0), "stochastic rounding is a transposed-form variant");
+    static_assert(!(PAIR && (SR || FR >= 0)), "pairs of the plain and rotated transposed forms only");
+    uint32_t bx = blockIdx.x;
+    if (PAIR && bx >= split) {  // uniform across the workgroup
+        bx -= split;
+        x = x1; ldx = ldx1; rows = rows1; cols = cols1; codes = codes1; scales = scales1;
+    }
     constexpr int BB = F == E2M1 ? 16 : 32;             // code bytes per block of one output row
     constexpr int CB = kTrBlocks * BB;                  // staged bytes per output row: 128 or 256
     constexpr int NCH = CB / 16;                        // 16-byte chunks per output row
@@ -293,7 +317,7 @@ __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t ctile = (int64_t)blockIdx.x * kTrCols;
+    const int64_t ctile = (int64_t)bx * kTrCols;
     const int64_t rb0 = (int64_t)blockIdx.y * kTrBlocks;
     const int64_t nrb = rows / 32;
     const int nb = (int)((nrb - rb0) < kTrBlocks ? (nrb - rb0) : kTrBlocks);    // valid blocks

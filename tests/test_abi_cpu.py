@@ -26,6 +26,7 @@ def L():
     lib.mx_hadamard32_quantize.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
     lib.mx_quantize_dual.argtypes = [P, i64, i64, i64, i32, P, P, i32, i32, u32, P, P, P]
     lib.mx_quantize_transpose_sr.argtypes = [P, i64, i64, i64, i32, u32, ctypes.c_uint64, i32, P, P, P]
+    lib.mx_quantize_pair.argtypes = [i32, i32, u32, P, i64, i64, i64, P, P, P, i64, i64, i64, P, P, P]
     lib.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
     lib.mx_status_string.argtypes = [ctypes.c_int]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -40,7 +41,8 @@ def declared_functions():
 def test_exports_every_declared_function(L):
     names = declared_functions()
     assert {"mx_quantize", "mx_quantize_transpose", "mx_hadamard32_quantize", "mx_quantize_dual",
-            "mx_quantize_transpose_sr", "mx_gemm", "mx_status_string", "mx_version"} <= set(names)
+            "mx_quantize_transpose_sr", "mx_quantize_pair", "mx_gemm", "mx_status_string",
+            "mx_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), "libmx.so does not export %s" % n
 
@@ -107,6 +109,27 @@ def test_dual_rejects(L):
     assert f(*args(ldx=63)) == INVALID
     assert f(*args(x=None)) == INVALID
     assert f(*args(rows=0, x=None, cr=None, sr=None, ct=None, st=None)) == OK
+
+
+def test_pair_rejects(L):
+    f = L.mx_quantize_pair
+    X1, C1, S1 = P(0x60000000), P(0x70000000), P(0x78000000)
+    args = lambda **k: [k.get("mode", 0), k.get("fmt", E4M3), 0,
+                        k.get("x0", X), k.get("r0", 64), k.get("c0", 64), k.get("l0", 64), k.get("cd0", C),
+                        k.get("s0", S), k.get("x1", X1), k.get("r1", 96), k.get("c1", 128), k.get("l1", 128),
+                        k.get("cd1", C1), k.get("s1", S1), None]
+    assert f(*args(mode=3)) == INVALID                   # unknown mode
+    assert f(*args(fmt=7)) == INVALID
+    assert f(*args(c1=48, l1=48)) == INVALID             # row mode: cols % 32 of the second tensor
+    assert f(*args(mode=1, r0=48)) == INVALID            # transposed modes: rows % 32
+    assert f(*args(mode=2, r1=40)) == INVALID
+    assert f(*args(l0=63)) == INVALID                    # ldx < cols
+    assert f(*args(x1=None)) == INVALID
+    assert f(*args(cd1=P(0x20000100))) == INVALID        # second codes inside the first codes
+    assert f(*args(s1=P(0x30000010))) == INVALID         # second scales inside the first scales
+    assert f(*args(cd0=P(0x60000000))) == INVALID        # first codes over the second input
+    assert f(*args(s1=P(0x10000040))) == INVALID         # second scales over the first input
+    assert f(*args(r0=0, r1=0, x0=None, x1=None, cd0=None, s0=None, cd1=None, s1=None)) == OK  # both empty
 
 
 def test_gemm_rejects(L):
