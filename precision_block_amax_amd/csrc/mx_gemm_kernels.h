@@ -961,19 +961,29 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                                                                   sRb[wn * 64 + j * 32 + 8 * q + 4 * h + e] - 254);
         return v;
     };
-    if constexpr (RBA == 128 && RBB == 128) {
-        // Stage the wave's 128 x 64 tile of C through LDS (16 KiB per wave in
-        // the stage buffers, free once every wave has left the main loop) and
-        // write it back with consecutive lanes covering whole 128-byte (bf16)
-        // or 256-byte (fp32) row segments.  16-byte chunks are XOR-swizzled by
-        // the row so the column-wise writes spread over the banks.  fp32 output
-        // goes in two passes of 64 rows.
+    if constexpr (RBA == 128 || RBB == 128) {
+        // Stage the wave's 128 x 64 tile of C through LDS (the stage buffers,
+        // free once every wave has left the main loop) and write it back with
+        // consecutive lanes covering whole 128-byte (bf16) or 256-byte (fp32)
+        // row segments.  16-byte chunks are XOR-swizzled by the row so the
+        // column-wise writes spread over the banks.  With 128-byte rows in
+        // both operands' stage buffers every wave has 16 KiB (bf16 in one pass
+        // of 128 rows, fp32 in two of 64); with one E2M1 operand (64-byte rows)
+        // the two 32 KiB buffers of the other give each wave 8 KiB (passes of
+        // 64 or 32 rows).
         barrier();
-        uint8_t *reg = ((wave >> 1) == 0 ? sA0 : (wave >> 1) == 1 ? sA1 : (wave >> 1) == 2 ? sB0 : sB1) + (wave & 1) * 16384;
+        constexpr int REG = (RBA == 128 && RBB == 128) ? 16384 : 8192;  // bytes per wave
+        uint8_t *reg;
+        if constexpr (REG == 16384)
+            reg = ((wave >> 1) == 0 ? sA0 : (wave >> 1) == 1 ? sA1 : (wave >> 1) == 2 ? sB0 : sB1) + (wave & 1) * 16384;
+        else if constexpr (RBA == 128)
+            reg = (wave < 4 ? sA0 : sA1) + (wave & 3) * 8192;
+        else
+            reg = (wave < 4 ? sB0 : sB1) + (wave & 3) * 8192;
         constexpr int ESZ = BF16OUT ? 2 : 4;
         constexpr int ROWB = 64 * ESZ;             // bytes per row of the wave's tile
         constexpr int CPR = ROWB / 16;             // 16-byte chunks per row: 8 or 16
-        constexpr int PASS_ROWS = 16384 / ROWB;    // rows per pass: 128 or 64
+        constexpr int PASS_ROWS = REG / ROWB;      // rows per pass: 128, 64 or 32
         constexpr int PASSES = 128 / PASS_ROWS;
         const int mbase = m0 + wm * 128, nbase = n0 + wn * 64;
         const bool full_cols = nbase + 64 <= g.N;
