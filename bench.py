@@ -51,6 +51,8 @@ PROFILE_COMMANDS = (
     "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
     "rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/prof_clock -o clock -- "
     "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "rocprofv3 --pmc MfmaUtil --output-format csv -d gpurun_out/prof_mfma -o mfma -- "
+    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
 )
 XCDS = 8          # MI355X: GRBM_GUI_ACTIVE sums the busy cycles of the 8 accelerator dies
 PEAK_SCLK_GHZ = 2.4
@@ -87,6 +89,13 @@ def measured_traffic(kernel: str):
     data = _profile_summary()
     k = None if data is None else data.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def measured_mfma_util(kernel: str):
+    """MFMA busy cycles as % of the SIMDs' cycles (rocprofv3 MfmaUtil) over the kernel's timed
+    step launches, from the committed counter summary, or None"""
+    data = _profile_summary()
+    return None if data is None else data.get("mfma_util_pct", {}).get(kernel)
 
 
 def measured_clock(kernel: str):
@@ -226,7 +235,7 @@ def _find(d, suffix):
 
 
 def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir: str, command: str,
-                       out_dir: str = os.path.join(ROOT, "profiles")) -> None:
+                       out_dir: str = os.path.join(ROOT, "profiles"), mfma_dir: str = None) -> None:
     """Turn rocprofv3 CSV output (kernel trace with stats; FETCH_SIZE and
     WRITE_SIZE counter passes with --calibrate-copy) into the short summaries
     kept under profiles/: per-kernel average durations, and HBM bytes per
@@ -355,9 +364,39 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
         lines.append("| `%s` | %d | %.1f | %.2f |" % (k, len(timed), us, sclk[k]))
     with open(os.path.join(out_dir, "sclk_%s.md" % WORKLOAD), "w") as f:
         f.write("\n".join(lines) + "\n")
+    # MFMA busy %: rocprofv3's MfmaUtil, the MFMA busy cycles summed over the SIMDs over
+    # (busy cycles of the busiest die x SIMDs), averaged over the kernel's timed step launches
+    mfma = {}
+    if mfma_dir is not None:
+        rows = sorted(_read_csv(_find(mfma_dir, "counter_collection.csv")), key=lambda r: int(r["Dispatch_Id"]))
+        first_m = next((int(r["Dispatch_Id"]) for r in rows if "reduce" in r["Kernel_Name"].lower()), None)
+        msteps = int(re.search(r"--steps (\d+)", command[4]).group(1))
+        perm = {}
+        for r in rows:
+            if r["Counter_Name"] != "MfmaUtil" or "mx::" not in r["Kernel_Name"]:
+                continue
+            if first_m is not None and int(r["Dispatch_Id"]) >= first_m:
+                continue
+            perm.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        lines = ["# MFMA busy per kernel (rocprofv3 MfmaUtil): %s" % WORKLOAD, "",
+                 "Command (from the repository root on the GPU box):", "", "    " + command[4], "",
+                 "MfmaUtil = MFMA busy cycles summed over the SIMDs / (busy cycles of the busiest die x SIMD "
+                 "count) x 100, averaged over each kernel's timed step launches (its last %d before the first "
+                 "cache fill). Kernels without matrix instructions read 0 and are left out." % msteps, "",
+                 "| kernel | timed launches | MFMA busy (%) |", "|---|---|---|"]
+        for k, v in sorted(perm.items(), key=lambda kv: kv[0]):
+            timed = v[-msteps:]
+            util = sum(timed) / len(timed)
+            if util <= 0.0:
+                continue
+            mfma[k] = util
+            lines.append("| `%s` | %d | %.1f |" % (k, len(timed), util))
+        with open(os.path.join(out_dir, "mfma_util_%s.md" % WORKLOAD), "w") as f:
+            f.write("\n".join(lines) + "\n")
     with open(os.path.join(out_dir, "traffic.json"), "w") as f:
         json.dump({"source_sha": kernel_source_sha(), "workload": WORKLOAD, "fetch_scale": f_scale,
-                   "write_scale": w_scale, "kernels": kern, "sclk_ghz": sclk, "commands": command[1:]}, f, indent=1)
+                   "write_scale": w_scale, "kernels": kern, "sclk_ghz": sclk, "mfma_util_pct": mfma,
+                   "commands": command[1:]}, f, indent=1)
 
 
 def ablation(mx, torch, seed: int) -> dict:
@@ -441,13 +480,17 @@ def main() -> int:
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table to stderr")
     ap.add_argument("--ablation", action="store_true",
                     help="only the weight-gradient rotation ablation (dW error of the Wgrad recipes)")
-    ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "CLOCK_DIR"),
-                    help="write profiles/ summaries from rocprofv3 CSV output and exit")
+    ap.add_argument("--summarize-profiles", nargs="+", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 CSV output (TRACE FETCH WRITE CLOCK [MFMA] "
+                         "directories) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 256 MiB device copy three times (HBM counter calibration)")
     args = ap.parse_args()
     if args.summarize_profiles:
-        summarize_profiles(*args.summarize_profiles, command=PROFILE_COMMANDS)
+        if len(args.summarize_profiles) not in (4, 5):
+            ap.error("--summarize-profiles takes the TRACE, FETCH, WRITE, CLOCK and optionally MFMA directories")
+        d = args.summarize_profiles
+        summarize_profiles(*d[:4], command=PROFILE_COMMANDS, mfma_dir=d[4] if len(d) == 5 else None)
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: the hot path runs on a single MI355X and this build "
@@ -671,6 +714,9 @@ def main() -> int:
     if sclk is not None:  # the profiled run's sustained clock: the peak the kernel could reach at it
         roofline["sclk_ghz"] = round(sclk, 3)
         roofline["frac_of_clock_adjusted_peak"] = round(dom["frac"] * PEAK_SCLK_GHZ / sclk, 4)
+    mfma_util = measured_mfma_util(kernel_symbol(dom["kernel"]))
+    if mfma_util is not None:  # the profiled run's MFMA busy share of the SIMD cycles
+        roofline["mfma_busy_pct"] = round(mfma_util, 1)
     q = [k for k in kernels if k["bound"] == "hbm"]
     quant_gbps = sum(k["work"] for k in q) / (sum(k["ms"] for k in q) * 1e-3) / 1e9
     quant_gbps_iso = sum(k["work"] for k in q) / (sum(k["isolated"]["ms"] for k in q) * 1e-3) / 1e9

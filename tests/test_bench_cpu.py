@@ -35,7 +35,8 @@ RUN = [
     (10, CALIB, 131072.0, 262144.0, 60000),  # 256 MiB calibration copies
     (11, CALIB, 131072.0, 262144.0, 60000),
 ]
-CMDS = ("trace --steps 2 --warmup 0", "fetch", "write", "clock --steps 2 --warmup 0")
+CMDS = ("trace --steps 2 --warmup 0", "fetch", "write", "clock --steps 2 --warmup 0",
+        "mfma --steps 2 --warmup 0")
 
 
 def _write(path, header, rows):
@@ -68,6 +69,9 @@ def profile_dirs(tmp_path):
     head = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
     for name, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"), ("GRBM_GUI_ACTIVE", "clock")):
         _write(str(tmp_path / sub / ("x_counter_collection.csv")), head, counters[name])
+    # MfmaUtil: 40 and 50 % for the step's two GEMM launches, 0 for the quantizer
+    mf = [[d, k, "MfmaUtil", (40.0 + 10.0 * (d == 4)) if k == GEMM else 0.0, 0, 1] for d, k, _, _, _ in RUN]
+    _write(str(tmp_path / "mfma" / "x_counter_collection.csv"), head, mf)
     return tmp_path
 
 
@@ -112,3 +116,13 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_mfma_summary(profile_dirs):
+    out = profile_dirs / "out2"
+    bench.summarize_profiles(*(str(profile_dirs / d) for d in ("trace", "fetch", "write", "clock")),
+                             command=CMDS, out_dir=str(out), mfma_dir=str(profile_dirs / "mfma"))
+    data = json.load(open(out / "traffic.json"))
+    # the mean over the step's two GEMM launches (40 and 50); kernels reading 0 are left out
+    assert data["mfma_util_pct"] == {GEMM: pytest.approx(45.0)}
+    assert "| 2 | 45.0 |" in open(out / ("mfma_util_%s.md" % bench.WORKLOAD)).read()
