@@ -43,15 +43,15 @@ PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
 CONFIGS = (1, 2, 3)  # the three Llama-3.1-8B workloads
 WORKLOAD = "llama31_8b_linear_set"
 PROFILE_COMMANDS = (
-    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace -- "
+    "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/prof_trace -o trace -- "
     "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch -- "
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/prof_fetch -o fetch -- "
     "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write -- "
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/prof_write -o write -- "
     "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
-    "rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/prof_clock -o clock -- "
+    "rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d rocprof_out/prof_clock -o clock -- "
     "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
-    "rocprofv3 --pmc MfmaUtil --output-format csv -d gpurun_out/prof_mfma -o mfma -- "
+    "rocprofv3 --pmc MfmaUtil --output-format csv -d rocprof_out/prof_mfma -o mfma -- "
     "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
 )
 XCDS = 8          # MI355X: GRBM_GUI_ACTIVE sums the busy cycles of the 8 accelerator dies
@@ -279,7 +279,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
     f_scale, w_scale = known_kib / f_copy, known_kib / w_copy
     os.makedirs(out_dir, exist_ok=True)
     lines = ["# rocprofv3 kernel trace: %s" % WORKLOAD, "",
-             "Command (from the repository root on the GPU box):", "", "    " + command[0], "",
+             "Command (run from the repository root on an MI355X):", "", "    " + command[0], "",
              "The library's kernels only (torch's kernels that fill the cache before each lone launch, "
              "and its copies, are left out; share is of the library's kernel time). Calls count the "
              "launches inside the step and the lone launches after a clean cache fill.", "",
@@ -314,7 +314,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
 
     kern = {}
     lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE): %s" % WORKLOAD, "",
-             "Commands (from the repository root on the GPU box), one counter per run:", "",
+             "Commands (run from the repository root on an MI355X), one counter per run:", "",
              "    " + command[1], "    " + command[2], "",
              "Calibration: a plain 256 MiB device copy (`%s`) reads FETCH_SIZE = %.0f KiB and "
              "WRITE_SIZE = %.0f KiB per dispatch for 262144 KiB read and written, so counter KiB are "
@@ -348,7 +348,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
             per.setdefault(r["Kernel_Name"], []).append((float(r["Counter_Value"]) / (XCDS * dt), dt))
     sclk = {}
     lines = ["# Sustained shader clock per kernel (rocprofv3 GRBM_GUI_ACTIVE): %s" % WORKLOAD, "",
-             "Command (from the repository root on the GPU box):", "", "    " + command[3], "",
+             "Command (run from the repository root on an MI355X):", "", "    " + command[3], "",
              "GRBM_GUI_ACTIVE sums the busy cycles of the %d dies; clock = value / (%d x dispatch time), "
              "averaged over the timed step launches (each kernel's last %d before the first cache fill). "
              "The dense peaks assume %.1f GHz. Kernels whose launches average under %d us are left out: "
@@ -379,7 +379,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
                 continue
             perm.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         lines = ["# MFMA busy per kernel (rocprofv3 MfmaUtil): %s" % WORKLOAD, "",
-                 "Command (from the repository root on the GPU box):", "", "    " + command[4], "",
+                 "Command (run from the repository root on an MI355X):", "", "    " + command[4], "",
                  "MfmaUtil = MFMA busy cycles summed over the SIMDs / (busy cycles of the busiest die x SIMD "
                  "count) x 100, averaged over each kernel's timed step launches (its last %d before the first "
                  "cache fill). Kernels without matrix instructions read 0 and are left out." % msteps, "",
@@ -493,7 +493,7 @@ def main() -> int:
         summarize_profiles(*d[:4], command=PROFILE_COMMANDS, mfma_dir=d[4] if len(d) == 5 else None)
         return 0
     if args.gpus != 1:
-        print("bench.py measures one GPU: the hot path runs on a single MI355X and this build "
+        print("bench.py measures one GPU: the hot path runs on a single MI355X and the library "
               "has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 

@@ -148,8 +148,8 @@ def test_gemm_rejects(L):
 
 def test_valid_call_without_a_device_reports_hip_error(L):
     """past validation the library asks HIP for the device; without one it
-    returns MX_ERR_HIP instead of crashing (on a GPU machine this would launch,
-    so it is skipped there)"""
+    returns MX_ERR_HIP instead of crashing (with a GPU present this would
+    launch, so it is skipped there)"""
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; the launch path is covered by the GPU tests")
