@@ -111,6 +111,21 @@ def test_shapes(mx, M, N, K):
     check_gemm(_host_c(_run(mx, qa, "e4m3", qb, "e2m1", False), False), C, S, False)
 
 
+@pytest.mark.parametrize("fa,fb,K", [("e2m1", "e2m1", 1024), ("e2m1", "e2m1", 1536), ("e4m3", "e4m3", 1536),
+                                     ("e4m3", "e2m1", 1024)])
+def test_second_round_k_order(mx, fa, fb, K):
+    """17 x 17 tiles of 256 x 256: more than one round on 256 CUs, and the
+    second round takes K's 16-byte scale slots (512 elements each) in
+    descending order: two or three slots of 256-K (E2M1 x E2M1) or 128-K
+    stages; every element within the tolerance"""
+    rng = np.random.default_rng(K + FMTS.index(fa) * 3 + FMTS.index(fb))
+    M = N = 17 * 256
+    qa, qb = _rand_operand(rng, M, K, fa), _rand_operand(rng, N, K, fb)
+    C, S = oracle.gemm(qa[0], qa[1], fa, qb[0], qb[1], fb)
+    print("case", fa, fb, M, N, K, flush=True)
+    check_gemm(_host_c(_run(mx, qa, fa, qb, fb, False), False), C, S, False)
+
+
 def test_ldc_and_zero_k(mx):
     import torch
     rng = np.random.default_rng(3)
