@@ -8,8 +8,8 @@
  *
  * What it computes, and where that is stated:
  *   - MX micro-scaling: a tensor is cut into 32-element blocks along the
- *     reduction dimension, each block carrying its own power-of-two scale
- *     ("MXFP4 ... 每塊配置獨立動態縮放指數": hzrcw.cc FP4-training article,
+ *     reduction dimension, each block carrying its own dynamic power-of-two
+ *     exponent (MXFP4 as described in the hzrcw.cc FP4-training article,
  *     section 02; block size 32: MindSpeed-LLM FSDP2 quantization page,
  *     recipe dynamic_MX-1-1-32 and --model.quant_block_size 32).
  *   - E4M3 / E5M2 element formats (Lumen page, section 1) and MXFP4 = E2M1

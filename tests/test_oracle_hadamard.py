@@ -12,7 +12,9 @@ stages h = 1, 2, 4, 8, 16 and c = RN32(1/sqrt 32).  Pins here:
   * on general inputs, |y - (H D x)/sqrt 32| stays within 8 * 2^-24 * c * sum|x|;
   * subnormal inputs survive (no flush to zero);
   * sign mask m on x equals mask 0 on diag(s) x, bit for bit;
-  * worked examples W8 / W9 and the transposed layout of the rotate-quantize call.
+  * worked examples W8 / W9 and the transposed layout of the rotate-quantize call;
+  * the fp32 stage order: hand-derived outputs (W11) of inputs on which running
+    any stage 2^b before a stage 2^a < 2^b rounds differently.
 """
 import decimal
 import json
@@ -143,6 +145,28 @@ def test_worked_examples_hadamard(orc, case):
     if "codes_first" in case:
         assert np.all(codes[:, 0] == int(case["codes_first"][0], 16))
         assert not codes[:, 1:].any()
+
+
+def _golden_order():
+    with open(GOLDEN) as f:
+        return json.load(f)["hadamard_order"]
+
+
+@pytest.mark.parametrize("case", _golden_order(), ids=lambda c: c["id"])
+def test_worked_examples_stage_order(orc, case):
+    """W11: every output's fp32 bits, as derived by hand for stages 1, 2, 4, 8, 16 ascending"""
+    x = np.zeros(32, dtype=np.uint32)
+    for i, h in case["x_f32"].items():
+        x[int(i)] = int(h, 16)
+    y = orc.hadamard32_f32(x.view(np.float32), case["mask"]).view(np.uint32)
+    a, b = case["a"], case["b"]
+    want = [int(case["y_by_bits"]["%d%d" % ((i >> a) & 1, (i >> b) & 1)], 16) for i in range(32)]
+    assert [int(v) for v in y] == want
+
+
+def test_stage_order_cases_cover_every_pair():
+    pairs = {(c["a"], c["b"]) for c in _golden_order()}
+    assert pairs == {(a, b) for a in range(5) for b in range(a + 1, 5)}
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
