@@ -92,6 +92,11 @@ typedef enum {
  * This is the Fprop operand quantizer (activations and weights stored with
  * the reduction dimension contiguous) and the Dgrad quantizer of the output
  * gradient.
+ * Defined by: FP4-training article on hzrcw.cc, section 02 (MX blocks, each
+ * with its own dynamic power-of-two exponent, on the forward and
+ * activation-gradient GEMM operands); MindSpeed-LLM FSDP2 page, section
+ * "三步启用 MXFP8 低精度训练" (block size 32 along the reduction dimension);
+ * Lumen page, section 1 (the E4M3 and E5M2 element formats).
  */
 mx_status_t mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
                         mx_format_t fmt, void *codes, void *scales, void *stream);
@@ -106,6 +111,10 @@ mx_status_t mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t 
  * Used for operands whose reduction dimension is strided in storage: the
  * weight in Dgrad (reduction over N_out) and, without rotation, the two
  * weight-gradient operands (reduction over tokens).
+ * Defined by: FP4-training article on hzrcw.cc, section 02 (the
+ * activation-gradient and weight-gradient GEMMs quantize their operands
+ * along the GEMM's own reduction dimension), with the block and formats of
+ * mx_quantize.
  */
 mx_status_t mx_quantize_transpose(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
                                   mx_format_t fmt, void *codes, void *scales, void *stream);
@@ -124,6 +133,11 @@ mx_status_t mx_quantize_transpose(const void *x_bf16, int64_t rows, int64_t cols
  * with the same output layout as mx_quantize_transpose.  Rotation blocks
  * coincide with the MX blocks.  sign_mask = 0 is the plain Sylvester
  * rotation.  Results are bit-identical for every launch configuration.
+ * Defined by: FP4-training article on hzrcw.cc, section 02 (one fixed,
+ * deterministic Hadamard rotation of both weight-gradient operands along
+ * tokens before the FP4 quantization, in place of random rotations).  The
+ * sign vector, stage order, constant and fp32 arithmetic are the readings
+ * written out above; the page gives the transform only in words.
  */
 mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
                                    uint32_t sign_mask, mx_format_t fmt, void *codes, void *scales,
@@ -214,6 +228,11 @@ mx_status_t mx_quantize_pair(mx_pair_mode_t mode, mx_format_t fmt, uint32_t sign
  * Dgrad: A = dY, B = W^T (from mx_quantize_transpose).  Wgrad: A = dY^T,
  * B = X^T (both from mx_hadamard32_quantize or mx_quantize_transpose).
  * Any pair of formats is accepted.
+ * Defined by: FP4-training article on hzrcw.cc, section 02 (the forward,
+ * activation-gradient and weight-gradient GEMMs on MX operands); Primus page,
+ * sections "性能瓶颈分析" and "GEMM 调优" (GEMM as the dominant training cost).
+ * A scale byte 0xFF (E8M0 NaN) makes every output element it contributes to
+ * NaN.
  */
 mx_status_t mx_gemm(const void *a_codes, const void *a_scales, mx_format_t fa,
                     const void *b_codes, const void *b_scales, mx_format_t fb,

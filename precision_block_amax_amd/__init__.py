@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "E4M3", "E5M2", "E2M1", "MXError", "lib", "library_path", "code_cols",
-    "quantize", "quantize_transpose", "hadamard32_quantize", "quantize_pair", "gemm",
+    "quantize", "quantize_transpose", "hadamard32_quantize", "quantize_dual",
+    "quantize_transpose_sr", "quantize_pair", "gemm",
 ]
 
 E4M3, E5M2, E2M1 = 0, 1, 2

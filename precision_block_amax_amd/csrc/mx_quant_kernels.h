@@ -28,14 +28,16 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
 // ---------------------------------------------------------------------------
 // Element casts by the gfx950 scaled conversions (v_cvt_scalef32_pk_*): they
 // convert v / scale, scale = 2^e, rounding to nearest with ties to even and
-// keeping the sign of zero.  E2M1 saturates to +-6, which is exactly the cast
-// of mx_convert.h.  E4M3 and E5M2 would round inputs just below the
+// keeping the sign of zero.  E2M1 saturates to +-6, which is exactly the
+// saturating MX cast.  E4M3 and E5M2 would round inputs just below the
 // saturation point up to the NaN / Inf code, so those values are first
-// clamped to +-max_normal * 2^e (one med3), after which the result equals
-// the mx_convert.h cast too.  Both facts were checked on the device against
-// mx_convert.h: every bf16 input at every reachable scale exponent, every
-// fp32 input at e = 0 and strided fp32 sweeps at nine exponents from -127
-// to 125, zero mismatches.  Element 2k goes to the low nibble / byte.
+// clamped to +-max_normal * 2^e (one med3), after which they equal the
+// saturating cast too.  Both facts were measured on the device against a
+// software cast (every bf16 input at every reachable scale exponent, every
+// fp32 input at e = 0 and strided fp32 sweeps at nine exponents from -127 to
+// 125, zero mismatches); the parity tests run every finite bf16 value at every
+// reachable scale through both quantizers.  Element 2k goes to the low
+// nibble / byte.
 typedef short v2s __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
