@@ -144,20 +144,73 @@ def test_ldc_and_zero_k(mx):
     assert np.all(to_host(z) == 0)
 
 
-def test_zero_and_nan_blocks(mx):
-    """an all-zero block contributes 0; a NaN-scale block (0xFF) makes its row NaN"""
-    import torch
-    rng = np.random.default_rng(8)
-    qa, qb = _rand_operand(rng, 64, 128, "e4m3"), _rand_operand(rng, 64, 128, "e4m3")
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m1", "e2m1"), ("e5m2", "e4m3"), ("e4m3", "e2m1")])
+@pytest.mark.parametrize("K", [352, 512, 1024])
+def test_zero_and_nan_blocks(mx, fa, fb, K):
+    """an all-zero block contributes exactly 0; an E8M0 NaN scale (0xFF) in row m of A
+    makes row m of C NaN, and one in row n of B makes column n NaN (K = 352: the
+    general kernels; K = 512 and 1024: the pipelined ones, with the NaN block in the
+    first and in a later scale slot)"""
+    rng = np.random.default_rng(8 + K + FMTS.index(fa) * 3 + FMTS.index(fb))
+    M, N = 300, 272
+    qa, qb = _rand_operand(rng, M, K, fa), _rand_operand(rng, N, K, fb)
     qa[0][3] = 0
     qa[1][3] = 0
-    C, S = oracle.gemm(qa[0], qa[1], "e4m3", qb[0], qb[1], "e4m3")
-    c = _host_c(_run(mx, qa, "e4m3", qb, "e4m3", False), False)
-    assert np.all(c[3] == 0)
-    check_gemm(c, C, S, False)
-    qa[1][5, 2] = 0xFF
-    c = _host_c(_run(mx, qa, "e4m3", qb, "e4m3", True), True)
-    assert np.all(np.isnan(c[5]))
+    C, S = oracle.gemm(qa[0], qa[1], fa, qb[0], qb[1], fb)
+    print("case", fa, fb, K, flush=True)
+    for bf16 in (False, True):
+        c = _host_c(_run(mx, qa, fa, qb, fb, bf16), bf16)
+        assert np.all(c[3] == 0)
+        check_gemm(c, C, S, bf16)
+    kb = K // 32
+    qa[1][5, 2] = 0xFF               # row 5 of A, block 2
+    qa[1][261, kb - 1] = 0xFF        # a row of the second tile row, last block
+    qb[1][7, kb // 2 + 1] = 0xFF     # row 7 of B (column 7 of C), a middle block
+    qb[1][270, 0] = 0xFF             # a column of the second tile column, block 0
+    C, S = oracle.gemm(qa[0], qa[1], fa, qb[0], qb[1], fb)
+    nan_rows, nan_cols = [5, 261], [7, 270]
+    for bf16 in (False, True):
+        c = _host_c(_run(mx, qa, fa, qb, fb, bf16), bf16)
+        assert np.all(np.isnan(c[nan_rows])), "NaN scale in A: row not NaN"
+        assert np.all(np.isnan(c[:, nan_cols])), "NaN scale in B: column not NaN"
+        keep_r = np.setdiff1d(np.arange(M), nan_rows)
+        keep_c = np.setdiff1d(np.arange(N), nan_cols)
+        sub = np.ix_(keep_r, keep_c)
+        check_gemm(c[sub], C[sub], S[sub], bf16)
+
+
+@pytest.mark.parametrize("M,N", [(300, 200), (257, 511), (40, 600)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_fp4_pipelined_tails(mx, M, N, bf16):
+    """E2M1 x E2M1 with K % 512 == 0 (the pipelined kernel) and M, N not multiples
+    of the 256 x 256 tile: rows past the edge read zeros through the buffer range
+    and the LDS-staged epilogue masks its stores; every element checked"""
+    rng = np.random.default_rng(M * 7 + N)
+    K = 1024
+    qa, qb = _rand_operand(rng, M, K, "e2m1"), _rand_operand(rng, N, K, "e2m1")
+    C, S = oracle.gemm(qa[0], qa[1], "e2m1", qb[0], qb[1], "e2m1")
+    print("case", M, N, K, "bf16" if bf16 else "f32", flush=True)
+    check_gemm(_host_c(_run(mx, qa, "e2m1", qb, "e2m1", bf16), bf16), C, S, bf16)
+
+
+def test_fp4_pipelined_tails_benchmark_shape(mx):
+    """the benchmark's FP4 tail case: the gate/up operands cut to 8000 x 28000 x 4096
+    (M and N ragged against the 256 x 256 tile), bf16 out; every row of the last,
+    partial tile row and a seeded sample of the others, against all N columns"""
+    cfg = workloads.config(2)
+    M, N = 8000, 28000
+    qa = tuple(t[:M] for t in _oracle_operands(cfg, "qX"))
+    qb = tuple(t[:N] for t in _oracle_operands(cfg, "qW"))
+    c = _host_c(_run(mx, qa, "e2m1", qb, "e2m1", True), True)
+    rng = np.random.default_rng(8000)
+    rows = np.unique(np.concatenate([np.arange(7936, M), rng.choice(7936, 448, replace=False)]))
+    worst = 0.0
+    for r0 in range(0, rows.size, 128):
+        rr = rows[r0:r0 + 128]
+        C, S = oracle.gemm(qa[0], qa[1], "e2m1", qb[0], qb[1], "e2m1", rows=rr)
+        worst = max(worst, check_gemm(c[rr], C, S, True))
+        print("rows %d of %d checked" % (min(r0 + 128, rows.size), rows.size), flush=True)
+    print("max |err|/S", worst, flush=True)
 
 
 FULL = [(1, "Y", True), (2, "Y", True), (3, "dW", False)]
@@ -220,7 +273,8 @@ def test_carrier_zero_stages_reference_scales(mx, fa, fb, K):
         check_gemm(c, C, S, bf16)
 
 
-@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e2m1"), ("e2m1", "e5m2")])
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e2m1"), ("e2m1", "e5m2"),
+                                   ("e2m1", "e2m1")])
 @pytest.mark.parametrize("spread", ["narrow", "full", "pathological"])
 def test_scale_spreads(mx, fa, fb, spread):
     """codes and E8M0 scales drawn directly: narrow spreads (carrier fast path),
