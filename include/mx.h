@@ -239,6 +239,50 @@ mx_status_t mx_gemm(const void *a_codes, const void *a_scales, mx_format_t fa,
                     int64_t M, int64_t N, int64_t K, void *c, mx_out_t out, int64_t ldc,
                     void *stream);
 
+/*
+ * mx_quantize_strided -- mx_quantize with row strides on the outputs: row r's
+ * codes go to codes + r * ld_codes and its scales to scales + r * ld_scales
+ * (bytes), with ld_codes >= the code bytes of a row (cols, or cols / 2 for
+ * E2M1) and ld_scales >= cols / 32.  Codes and scales may share one buffer as
+ * long as no byte is written twice: either their extents are disjoint, or
+ * ld_codes == ld_scales and each row's scales lie in the gap after its codes.
+ *
+ * FSDP2 low-precision all-gather payload (MindSpeed-LLM FSDP2 page, section
+ * "第 3 步：开启低精度 All-Gather", weights sharded along dim 0 as its
+ * "注意事项" requires): a rank quantizes its slab of weight rows [rows x K]
+ * (x = its rows, ldx = the full row) into ONE buffer of rows
+ *     [ codes (code_bytes(K)) | scales (K / 32) | 0 .. 15 bytes unused ],
+ * i.e. codes = payload, scales = payload + code_bytes(K), ld_codes =
+ * ld_scales = code_bytes(K) + K / 32 rounded up to a multiple of 16 (no
+ * padding when K % 512 == 0; 1.03125 bytes per element for FP8, 0.53125 for
+ * E2M1, against 2 for bf16).  K blocks never cross rows, so the
+ * ranks' payloads concatenated in rank order -- what an all-gather of one
+ * buffer per rank delivers -- are exactly the same layout for the whole
+ * weight, bit-identical to quantizing it in one call, and mx_gemm_strided
+ * takes them as an operand with those two strides, without a copy.
+ * Errors as mx_quantize.
+ */
+mx_status_t mx_quantize_strided(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt,
+                                void *codes, int64_t ld_codes, void *scales, int64_t ld_scales, void *stream);
+
+/*
+ * mx_gemm_strided -- mx_gemm on operands whose rows are strided: row m of A's
+ * codes starts at a_codes + m * lda and its scales at a_scales + m * ldsa
+ * (bytes), likewise for B with ldb and ldsb; lda >= code bytes of K
+ * elements and a multiple of 16 (code rows are read with 16-byte loads; the
+ * dense stride always is one), ldsa >= K / 32 (any value).  mx_gemm is the
+ * case lda = code bytes of K and ldsa = K / 32.  Used for the gathered FSDP2 payload (see
+ * mx_quantize_strided) and for operands that are row slices of larger
+ * buffers.  Scale strides that are multiples of 16 bytes, with 16-byte
+ * aligned code and dword-aligned scale pointers, keep the pipelined kernel
+ * (K % 512 == 0); other strides run the general kernels.
+ * Same tolerance as mx_gemm; with the same kernel the results are
+ * bit-identical to mx_gemm's on the same values.
+ */
+mx_status_t mx_gemm_strided(const void *a_codes, int64_t lda, const void *a_scales, int64_t ldsa, mx_format_t fa,
+                            const void *b_codes, int64_t ldb, const void *b_scales, int64_t ldsb, mx_format_t fb,
+                            int64_t M, int64_t N, int64_t K, void *c, mx_out_t out, int64_t ldc, void *stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char *mx_status_string(mx_status_t s);
 

@@ -22,7 +22,8 @@ import torch
 __all__ = [
     "E4M3", "E5M2", "E2M1", "MXError", "lib", "library_path", "code_cols",
     "quantize", "quantize_transpose", "hadamard32_quantize", "quantize_dual",
-    "quantize_transpose_sr", "quantize_pair", "gemm",
+    "quantize_transpose_sr", "quantize_pair", "gemm", "fsdp_payload", "payload_views",
+    "payload_width",
 ]
 
 E4M3, E5M2, E2M1 = 0, 1, 2
@@ -58,8 +59,11 @@ def lib() -> ctypes.CDLL:
         L.mx_quantize_transpose_sr.argtypes = [P, i64, i64, i64, i32, u32, ctypes.c_uint64, i32, P, P, P]
         L.mx_quantize_pair.argtypes = [i32, i32, u32, P, i64, i64, i64, P, P, P, i64, i64, i64, P, P, P]
         L.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
+        L.mx_quantize_strided.argtypes = [P, i64, i64, i64, i32, P, i64, P, i64, P]
+        L.mx_gemm_strided.argtypes = [P, i64, P, i64, i32, P, i64, P, i64, i32, i64, i64, i64, P, i32, i64, P]
         for fn in (L.mx_quantize, L.mx_quantize_transpose, L.mx_hadamard32_quantize, L.mx_quantize_dual,
-                   L.mx_quantize_transpose_sr, L.mx_quantize_pair, L.mx_gemm):
+                   L.mx_quantize_transpose_sr, L.mx_quantize_pair, L.mx_gemm, L.mx_quantize_strided,
+                   L.mx_gemm_strided):
             fn.restype = ctypes.c_int
         L.mx_status_string.argtypes = [ctypes.c_int]
         L.mx_status_string.restype = ctypes.c_char_p
@@ -118,15 +122,67 @@ def _ldx(x: torch.Tensor) -> int:
     return x.stride(0) if x.shape[0] > 1 else x.shape[1]
 
 
+def _row_strided(t: torch.Tensor, shape, device) -> int:
+    """row stride in bytes of a uint8 [rows x width] view with contiguous rows"""
+    if t.dtype != torch.uint8 or tuple(t.shape) != tuple(shape) or t.device != device:
+        raise ValueError("expected a uint8 tensor of shape %s on %s" % (tuple(shape), device))
+    if t.numel() and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
 def quantize(x: torch.Tensor, fmt, out=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """mx_quantize: blocks of 32 along the last dim; codes [R x C(/2)], scales [R x C/32]"""
+    """mx_quantize: blocks of 32 along the last dim; codes [R x C(/2)], scales [R x C/32].
+    `out` = (codes, scales) may be row-strided views (e.g. of an FSDP2 payload,
+    see fsdp_payload); those go through mx_quantize_strided."""
     _check_bf16_2d(x)
     f = _fmt(fmt)
     rows, cols = x.shape
+    if out is not None and not (out[0].is_contiguous() and out[1].is_contiguous()):
+        codes, scales = out
+        ldc = _row_strided(codes, (rows, code_cols(cols, f)), x.device)
+        lds = _row_strided(scales, (rows, cols // 32), x.device)
+        _check(lib().mx_quantize_strided(_ptr(x), rows, cols, _ldx(x), f, _ptr(codes), ldc, _ptr(scales), lds,
+                                         _stream(x.device, stream)))
+        return codes, scales
     codes, scales = _outputs(x.device, rows, cols, f, out)
     _check(lib().mx_quantize(_ptr(x), rows, cols, _ldx(x), f, _ptr(codes), _ptr(scales),
                              _stream(x.device, stream)))
     return codes, scales
+
+
+def payload_width(K: int, fmt) -> int:
+    """bytes per row of an FSDP2 payload: the row's codes, its K/32 scales, padded to 16"""
+    return (code_cols(K, _fmt(fmt)) + K // 32 + 15) // 16 * 16
+
+
+def payload_views(payload: torch.Tensor, K: int, fmt) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(codes, scales) views of an FSDP2 payload [rows x payload_width(K)]: each row holds a
+    weight row's codes followed by its scales (mx_quantize_strided)"""
+    cb = code_cols(K, _fmt(fmt))
+    if payload.dim() != 2 or payload.shape[1] != payload_width(K, fmt) or payload.dtype != torch.uint8:
+        raise ValueError("payload must be uint8 [rows x %d]" % payload_width(K, fmt))
+    return payload[:, :cb], payload[:, cb:cb + K // 32]
+
+
+def fsdp_payload(w_rows: torch.Tensor, fmt, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """One rank's FSDP2 all-gather payload: its slab of weight rows [rows x K] (dim-0 shard)
+    quantized into one buffer of rows [codes | scales].  The ranks' payloads concatenated in
+    rank order are the whole weight's payload; payload_views() of it is an mx_gemm operand."""
+    _check_bf16_2d(w_rows)
+    f = _fmt(fmt)
+    rows, K = w_rows.shape
+    width = payload_width(K, f)
+    if out is None:
+        out = torch.empty((rows, width), dtype=torch.uint8, device=w_rows.device)
+    elif out.dtype != torch.uint8 or tuple(out.shape) != (rows, width) or not out.is_contiguous():
+        raise ValueError("payload buffer must be contiguous uint8 [%d x %d]" % (rows, width))
+    codes, scales = payload_views(out, K, f)
+    ldp = width
+    _check(lib().mx_quantize_strided(_ptr(w_rows), rows, K, _ldx(w_rows), f, _ptr(codes), ldp, _ptr(scales), ldp,
+                                     _stream(w_rows.device, stream)))
+    return out
 
 
 def quantize_transpose(x: torch.Tensor, fmt, out=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -211,25 +267,32 @@ def quantize_pair(mode: str, x0: torch.Tensor, x1: torch.Tensor, fmt, sign_mask:
 def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, fa, b_codes: torch.Tensor,
          b_scales: torch.Tensor, fb, out_dtype: torch.dtype = torch.bfloat16,
          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """mx_gemm: C[M x N] = A[M x K] . B[N x K]^T on MX operands"""
+    """mx_gemm: C[M x N] = A[M x K] . B[N x K]^T on MX operands.  Operands may be
+    row-strided uint8 views (rows contiguous), e.g. payload_views() of a gathered
+    FSDP2 payload; those go through mx_gemm_strided."""
     fa_, fb_ = _fmt(fa), _fmt(fb)
     M, kb = a_scales.shape
     N, kb2 = b_scales.shape
     K = 32 * kb
     if kb2 != kb:
         raise ValueError("A and B disagree on K")
-    for t, shp in ((a_codes, (M, code_cols(K, fa_))), (b_codes, (N, code_cols(K, fb_))),
-                   (a_scales, (M, kb)), (b_scales, (N, kb))):
-        if t.dtype != torch.uint8 or tuple(t.shape) != shp or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("operand must be contiguous uint8 of shape %s on a GPU" % (shp,))
+    dev = a_codes.device
+    if not a_codes.is_cuda:
+        raise ValueError("operands must be on a GPU")
+    lds = [_row_strided(t, shp, dev) for t, shp in ((a_codes, (M, code_cols(K, fa_))), (a_scales, (M, kb)),
+                                                     (b_codes, (N, code_cols(K, fb_))), (b_scales, (N, kb)))]
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be float32 or bfloat16")
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
     elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.stride(1) != 1:
         raise ValueError("bad output buffer")
     ldc = out.stride(0) if M > 1 else N
-    _check(lib().mx_gemm(_ptr(a_codes), _ptr(a_scales), fa_, _ptr(b_codes), _ptr(b_scales), fb_,
-                         M, N, K, _ptr(out), OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, ldc,
-                         _stream(a_codes.device, stream)))
+    o = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    if all(t.is_contiguous() for t in (a_codes, a_scales, b_codes, b_scales)):
+        _check(lib().mx_gemm(_ptr(a_codes), _ptr(a_scales), fa_, _ptr(b_codes), _ptr(b_scales), fb_,
+                             M, N, K, _ptr(out), o, ldc, _stream(dev, stream)))
+    else:
+        _check(lib().mx_gemm_strided(_ptr(a_codes), lds[0], _ptr(a_scales), lds[1], fa_, _ptr(b_codes), lds[2],
+                                     _ptr(b_scales), lds[3], fb_, M, N, K, _ptr(out), o, ldc, _stream(dev, stream)))
     return out

@@ -65,6 +65,53 @@ mx_status_t check_quant(const void *x, int64_t rows, int64_t cols, int64_t ldx, 
 
 mx_status_t launched(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
+// Two strided row patterns, `rows` rows each: row i of the first covers bytes
+// [p + i * lp, p + i * lp + wp), row j of the second [q + j * lq, q + j * lq + wq).
+// They are disjoint if their whole extents are, or if they share one stride L
+// and, within every period of L bytes, the second's row sits in the gap after
+// the first's (the layout of rows of [codes | scales] in one buffer).
+bool strided_overlap(const void *p, int64_t lp, int64_t wp, const void *q, int64_t lq, int64_t wq, int64_t rows) {
+    if (rows <= 0 || wp <= 0 || wq <= 0) return false;
+    if (!overlap(p, (rows - 1) * lp + wp, q, (rows - 1) * lq + wq)) return false;
+    if (lp != lq) return true;
+    const int64_t L = lp;
+    int64_t d = (int64_t)((uintptr_t)q - (uintptr_t)p) % L;
+    if (d < 0) d += L;
+    return !(d >= wp && d + wq <= L);
+}
+
+// checks of the GEMM's arguments, operand row strides in bytes
+mx_status_t check_gemm(const void *a_codes, int64_t lda, const void *a_scales, int64_t ldsa, int fa,
+                       const void *b_codes, int64_t ldb, const void *b_scales, int64_t ldsb, int fb, int64_t M,
+                       int64_t N, int64_t K, const void *c, int out, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MX_ERR_INVALID_ARG;
+    if (!fmt_ok(fa) || !fmt_ok(fb) || (out != MX_OUT_F32 && out != MX_OUT_BF16)) return MX_ERR_INVALID_ARG;
+    if (ldc < N) return MX_ERR_INVALID_ARG;
+    if (lda < code_bytes(K, fa) || ldb < code_bytes(K, fb) || ldsa < K / 32 || ldsb < K / 32)
+        return MX_ERR_INVALID_ARG;
+    // code rows are read with 16-byte loads (dense rows always qualify: K % 32 == 0)
+    if (lda % 16 != 0 || ldb % 16 != 0) return MX_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MX_OK;
+    if (!c) return MX_ERR_INVALID_ARG;
+    if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return MX_ERR_INVALID_ARG;
+    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
+        return MX_ERR_UNSUPPORTED;
+    if ((M + 255) / 256 * ((N + 255) / 256) >= ((int64_t)1 << 31)) return MX_ERR_UNSUPPORTED;
+    if (M - 1 > (INT64_MAX - N) / ldc) return MX_ERR_INVALID_ARG;
+    if (K > 0 && ((M - 1) > INT64_MAX / lda || (N - 1) > INT64_MAX / ldb || (M - 1) > INT64_MAX / ldsa ||
+                  (N - 1) > INT64_MAX / ldsb))
+        return MX_ERR_INVALID_ARG;
+    const int64_t cbytes = ((M - 1) * ldc + N) * (out == MX_OUT_BF16 ? 2 : 4);
+    if (K > 0) {
+        const int64_t ab = (M - 1) * lda + code_bytes(K, fa), bb = (N - 1) * ldb + code_bytes(K, fb);
+        const int64_t asb = (M - 1) * ldsa + K / 32, bsb = (N - 1) * ldsb + K / 32;
+        if (overlap(c, cbytes, a_codes, ab) || overlap(c, cbytes, a_scales, asb) ||
+            overlap(c, cbytes, b_codes, bb) || overlap(c, cbytes, b_scales, bsb))
+            return MX_ERR_INVALID_ARG;
+    }
+    return MX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,29 +224,42 @@ mx_status_t mx_quantize_pair(mx_pair_mode_t mode, mx_format_t fmt, uint32_t sign
 mx_status_t mx_gemm(const void *a_codes, const void *a_scales, mx_format_t fa, const void *b_codes,
                     const void *b_scales, mx_format_t fb, int64_t M, int64_t N, int64_t K, void *c,
                     mx_out_t out, int64_t ldc, void *stream) {
-    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MX_ERR_INVALID_ARG;
-    if (!fmt_ok(fa) || !fmt_ok(fb) || (out != MX_OUT_F32 && out != MX_OUT_BF16)) return MX_ERR_INVALID_ARG;
-    if (ldc < N) return MX_ERR_INVALID_ARG;
-    if (M == 0 || N == 0) return MX_OK;
-    if (!c) return MX_ERR_INVALID_ARG;
-    if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return MX_ERR_INVALID_ARG;
-    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
-        return MX_ERR_UNSUPPORTED;
-    if ((M + 255) / 256 * ((N + 255) / 256) >= ((int64_t)1 << 31)) return MX_ERR_UNSUPPORTED;
-    if (M - 1 > (INT64_MAX - N) / ldc) return MX_ERR_INVALID_ARG;
-    const int64_t cbytes = ((M - 1) * ldc + N) * (out == MX_OUT_BF16 ? 2 : 4);
-    if (K > 0) {
-        const int64_t ab = M * code_bytes(K, fa), bb = N * code_bytes(K, fb);
-        const int64_t asb = M * (K / 32), bsb = N * (K / 32);
-        if (overlap(c, cbytes, a_codes, ab) || overlap(c, cbytes, a_scales, asb) ||
-            overlap(c, cbytes, b_codes, bb) || overlap(c, cbytes, b_scales, bsb))
-            return MX_ERR_INVALID_ARG;
-    }
+    if (!fmt_ok(fa) || !fmt_ok(fb) || K < 0) return MX_ERR_INVALID_ARG;
+    return mx_gemm_strided(a_codes, code_bytes(K, fa), a_scales, K / 32, fa, b_codes, code_bytes(K, fb), b_scales,
+                           K / 32, fb, M, N, K, c, out, ldc, stream);
+}
+
+mx_status_t mx_gemm_strided(const void *a_codes, int64_t lda, const void *a_scales, int64_t ldsa, mx_format_t fa,
+                            const void *b_codes, int64_t ldb, const void *b_scales, int64_t ldsb, mx_format_t fb,
+                            int64_t M, int64_t N, int64_t K, void *c, mx_out_t out, int64_t ldc, void *stream) {
+    mx_status_t st = check_gemm(a_codes, lda, a_scales, ldsa, fa, b_codes, ldb, b_scales, ldsb, fb, M, N, K, c, out,
+                                ldc);
+    if (st != MX_OK || M == 0 || N == 0) return st;
+    if ((st = check_device()) != MX_OK) return st;
+    return launched(mx::launch_gemm((const uint8_t *)a_codes, lda, (const uint8_t *)a_scales, ldsa, fa,
+                                    (const uint8_t *)b_codes, ldb, (const uint8_t *)b_scales, ldsb, fb, M, N, K, c,
+                                    out == MX_OUT_BF16, ldc, (hipStream_t)stream));
+}
+
+mx_status_t mx_quantize_strided(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt,
+                                void *codes, int64_t ld_codes, void *scales, int64_t ld_scales, void *stream) {
+    if (rows < 0 || cols < 0 || !fmt_ok(fmt) || cols % 32 != 0 || ldx < cols) return MX_ERR_INVALID_ARG;
+    const int64_t cbr = code_bytes(cols, fmt), sbr = cols / 32;
+    if (ld_codes < cbr || ld_scales < sbr) return MX_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return MX_OK;
+    if (!x_bf16 || !codes || !scales) return MX_ERR_INVALID_ARG;
+    if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31) return MX_ERR_UNSUPPORTED;
+    if (rows > INT64_MAX / ldx || rows > INT64_MAX / ld_codes || rows > INT64_MAX / ld_scales)
+        return MX_ERR_INVALID_ARG;
+    if ((rows * cols) / 8 >= ((int64_t)1 << 32)) return MX_ERR_UNSUPPORTED;
+    const int64_t xb = ((rows - 1) * ldx + cols) * 2;
+    if (overlap(x_bf16, xb, codes, (rows - 1) * ld_codes + cbr) || overlap(x_bf16, xb, scales, (rows - 1) * ld_scales + sbr) ||
+        strided_overlap(codes, ld_codes, cbr, scales, ld_scales, sbr, rows))
+        return MX_ERR_INVALID_ARG;
     mx_status_t st = check_device();
     if (st != MX_OK) return st;
-    return launched(mx::launch_gemm((const uint8_t *)a_codes, (const uint8_t *)a_scales, fa,
-                                    (const uint8_t *)b_codes, (const uint8_t *)b_scales, fb, M, N, K, c,
-                                    out == MX_OUT_BF16, ldc, (hipStream_t)stream));
+    return launched(mx::launch_quantize_rows_strided((const uint16_t *)x_bf16, rows, cols, ldx, fmt, (uint8_t *)codes,
+                                                     ld_codes, (uint8_t *)scales, ld_scales, (hipStream_t)stream));
 }
 
 }  // extern "C"

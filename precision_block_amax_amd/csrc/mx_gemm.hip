@@ -11,8 +11,9 @@ MX_PAIR(1, 0) MX_PAIR(1, 1) MX_PAIR(1, 2)
 MX_PAIR(2, 0) MX_PAIR(2, 1) MX_PAIR(2, 2)
 #undef MX_PAIR
 
-hipError_t launch_gemm(const uint8_t *a, const uint8_t *as, int fa, const uint8_t *b, const uint8_t *bs, int fb,
-                       int64_t M, int64_t N, int64_t K, void *c, bool bf16_out, int64_t ldc, hipStream_t stream) {
+hipError_t launch_gemm(const uint8_t *a, int64_t lda, const uint8_t *as, int64_t ldsa, int fa, const uint8_t *b,
+                       int64_t ldb, const uint8_t *bs, int64_t ldsb, int fb, int64_t M, int64_t N, int64_t K, void *c,
+                       bool bf16_out, int64_t ldc, hipStream_t stream) {
     if (K == 0) {
         const int64_t n = M * N;
         const dim3 grid((unsigned)((n + 255) / 256));
@@ -24,6 +25,7 @@ hipError_t launch_gemm(const uint8_t *a, const uint8_t *as, int fa, const uint8_
     }
     GemmArgs g;
     g.a = a; g.as = as; g.b = b; g.bs = bs; g.c = c; g.ldc = ldc;
+    g.lda = lda; g.ldsa = ldsa; g.ldb = ldb; g.ldsb = ldsb;
     g.M = (int)M; g.N = (int)N; g.K = (int)K;
     g.tiles_m = (int)((M + BM - 1) / BM);
     g.tiles_n = (int)((N + BN - 1) / BN);

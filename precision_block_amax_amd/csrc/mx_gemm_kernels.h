@@ -53,10 +53,14 @@
 
 namespace mx {
 
+// Operand rows are strided: row r of A's codes starts at a + r * lda and its
+// scales at as + r * ldsa (bytes); the dense layout has lda = K (FP8) or K / 2
+// (E2M1) and ldsa = K / 32.
 struct GemmArgs {
     const uint8_t *a, *as, *b, *bs;
     void *c;
     int64_t ldc;
+    int64_t lda, ldsa, ldb, ldsb;
     int M, N, K;
     int tiles_m, tiles_n;
 };
@@ -144,25 +148,25 @@ struct Stager {
             const int id = tid + NT * i, row = id / CPRA, ch = id % CPRA;
             const int gr = min(m0 + row, g.M - 1);
             const int64_t off = (int64_t)kt * RBA + ch * 16;
-            ra[i] = off < rowA ? *reinterpret_cast<const uint4 *>(g.a + gr * rowA + off) : make_uint4(0, 0, 0, 0);
+            ra[i] = off < rowA ? *reinterpret_cast<const uint4 *>(g.a + gr * g.lda + off) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < NLB; i++) {
             const int id = tid + NT * i, row = id / CPRB, ch = id % CPRB;
             const int gr = min(n0 + row, g.N - 1);
             const int64_t off = (int64_t)kt * RBB + ch * 16;
-            rb[i] = off < rowB ? *reinterpret_cast<const uint4 *>(g.b + gr * rowB + off) : make_uint4(0, 0, 0, 0);
+            rb[i] = off < rowB ? *reinterpret_cast<const uint4 *>(g.b + gr * g.ldb + off) : make_uint4(0, 0, 0, 0);
         }
         // scales: thread t owns row t of the A and B tiles
         const int ga = min(m0 + tid, g.M - 1), gb = min(n0 + tid, g.N - 1);
         const int kb0 = kt * SB;
         if (scale_vec && kb0 + SB <= kblocks) {
             if constexpr (SB == 4) {
-                rsa[0] = *reinterpret_cast<const uint32_t *>(g.as + (int64_t)ga * kblocks + kb0);
-                rsb[0] = *reinterpret_cast<const uint32_t *>(g.bs + (int64_t)gb * kblocks + kb0);
+                rsa[0] = *reinterpret_cast<const uint32_t *>(g.as + ga * g.ldsa + kb0);
+                rsb[0] = *reinterpret_cast<const uint32_t *>(g.bs + gb * g.ldsb + kb0);
             } else {
-                const uint2 ta = *reinterpret_cast<const uint2 *>(g.as + (int64_t)ga * kblocks + kb0);
-                const uint2 tb = *reinterpret_cast<const uint2 *>(g.bs + (int64_t)gb * kblocks + kb0);
+                const uint2 ta = *reinterpret_cast<const uint2 *>(g.as + ga * g.ldsa + kb0);
+                const uint2 tb = *reinterpret_cast<const uint2 *>(g.bs + gb * g.ldsb + kb0);
                 rsa[0] = ta.x; rsa[1] = ta.y;
                 rsb[0] = tb.x; rsb[1] = tb.y;
             }
@@ -174,8 +178,8 @@ struct Stager {
                 for (int t = 0; t < 4; t++) {
                     const int kb = kb0 + 4 * q + t;
                     if (kb < kblocks) {
-                        va |= (uint32_t)g.as[(int64_t)ga * kblocks + kb] << (8 * t);
-                        vb |= (uint32_t)g.bs[(int64_t)gb * kblocks + kb] << (8 * t);
+                        va |= (uint32_t)g.as[ga * g.ldsa + kb] << (8 * t);
+                        vb |= (uint32_t)g.bs[gb * g.ldsb + kb] << (8 * t);
                     }
                 }
                 rsa[q] = va;
@@ -233,7 +237,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fp4(GemmArgs g) {
     const int64_t rowA = g.K / 2, rowB = g.K / 2;
     const int kblocks = g.K / 32;
     const int ntk = (g.K + BK - 1) / BK;
-    const bool scale_vec = (kblocks % SB == 0) && (((uintptr_t)g.as | (uintptr_t)g.bs) % SB == 0);
+    const bool scale_vec = (kblocks % SB == 0) && (((uintptr_t)g.as | (uintptr_t)g.bs) % SB == 0) &&
+                           ((g.ldsa | g.ldsb) % SB == 0);
 
     Stager<RB, RB, SB> st;
     v16f acc[4][4];
@@ -365,7 +370,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_carrier(GemmArgs g) {
     const int64_t rowA = FA == E2M1 ? g.K / 2 : g.K, rowB = FB == E2M1 ? g.K / 2 : g.K;
     const int kblocks = g.K / 32;
     const int ntk = (g.K + BK - 1) / BK;
-    const bool scale_vec = (kblocks % SB == 0) && (((uintptr_t)g.as | (uintptr_t)g.bs) % SB == 0);
+    const bool scale_vec = (kblocks % SB == 0) && (((uintptr_t)g.as | (uintptr_t)g.bs) % SB == 0) &&
+                           ((g.ldsa | g.ldsb) % SB == 0);
 
     // reference scales R = max over the row's blocks; the tile is "wide" if a
     // row's scales spread over more than kSpreadMax binades or hold 0xFF
@@ -373,7 +379,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_carrier(GemmArgs g) {
     {
         const int ga = min(m0 + tid, g.M - 1), gb = min(n0 + tid, g.N - 1);
         int amax = 0, amin = 255, bmax = 0, bmin = 255;
-        const uint8_t *pa = g.as + (int64_t)ga * kblocks, *pb = g.bs + (int64_t)gb * kblocks;
+        const uint8_t *pa = g.as + ga * g.ldsa, *pb = g.bs + gb * g.ldsb;
         for (int kb = 0; kb < kblocks; kb++) {
             const int a = pa[kb], b = pb[kb];
             amax = max(amax, a); amin = min(amin, a);
@@ -675,16 +681,17 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     // order of the fp32 sum over K changes.
     const bool krev = ((blockIdx.x >> 3) / kCusPerXcd) & 1;
 
-    const int rowA = A4 ? g.K / 2 : g.K, rowB = B4 ? g.K / 2 : g.K;
+    // row strides in bytes (the launcher keeps 256 rows of either operand below 2^31 bytes)
+    const int rowA = (int)g.lda, rowB = (int)g.ldb, srowA = (int)g.ldsa, srowB = (int)g.ldsb;
     const int kblocks = g.K / 32;
     const int ntk = g.K / KE;
     const int mrows = min(BM, g.M - m0), nrows = min(BN, g.N - n0);
     const uint32_t nrecA = (uint32_t)mrows * rowA, nrecB = (uint32_t)nrows * rowB;
-    const uint32_t nrecSA = (uint32_t)mrows * kblocks, nrecSB = (uint32_t)nrows * kblocks;
+    const uint32_t nrecSA = (uint32_t)mrows * srowA, nrecSB = (uint32_t)nrows * srowB;
     const v4i rA = rsrc(g.a + (int64_t)m0 * rowA, nrecA);
     const v4i rB = rsrc(g.b + (int64_t)n0 * rowB, nrecB);
-    const v4i rSA = rsrc(g.as + (int64_t)m0 * kblocks, nrecSA);
-    const v4i rSB = rsrc(g.bs + (int64_t)n0 * kblocks, nrecSB);
+    const v4i rSA = rsrc(g.as + (int64_t)m0 * srowA, nrecSA);
+    const v4i rSB = rsrc(g.bs + (int64_t)n0 * srowB, nrecSB);
 
     // carrier: reference scale per row and the tile's path (threads 0..255:
     // rows of A, 256..511: rows of B).  The fast kernel (MODE 1) leaves a tile
@@ -701,9 +708,10 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
         const bool isA = tid < BM;
         const int r = isA ? tid : tid - BM;
         const int gr = isA ? min(m0 + r, g.M - 1) : min(n0 + r, g.N - 1);
-        const bool vec = (kblocks % 16 == 0) && ((((uintptr_t)g.as | (uintptr_t)g.bs) & 15) == 0);
+        const bool vec = (kblocks % 16 == 0) && ((((uintptr_t)g.as | (uintptr_t)g.bs) & 15) == 0) &&
+                         (((srowA | srowB) & 15) == 0);
         int mx_, mn_;
-        row_scale_range((isA ? g.as : g.bs) + (int64_t)gr * kblocks, kblocks, vec, mx_, mn_);
+        row_scale_range((isA ? g.as : g.bs) + (int64_t)gr * (isA ? srowA : srowB), kblocks, vec, mx_, mn_);
         (isA ? sRa : sRb)[r] = mx_;
         const bool w = mx_ - mn_ > kSpreadMax || mx_ == 255;
         if (__syncthreads_or(w) != 0) {  // uniform across the workgroup
@@ -717,23 +725,26 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     // l % CPR of row seg * (64 / CPR) + l / CPR, i.e. logical chunk pch ^ key.
     // Instruction q's rows are instruction 0's plus q * 64 / CPR: the row part
     // is a uniform (scalar) offset, and the swizzle key of 128-byte rows moves
-    // by 8 rows -> key ^ 4, i.e. byte offset ^ 64, on odd q (row strides are
-    // multiples of 128 bytes, so bit 6 belongs to the chunk part); the keys of
-    // 64- and 32-byte rows do not change.
+    // by 8 rows -> key ^ 4 on odd q; the keys of 64- and 32-byte rows do not
+    // change.
     static_assert(64 / CPRA == 8 || RBA < 128, "8 rows per instruction");
     static_assert(64 / CPRB == 8 || RBB < 128, "8 rows per instruction");
     const int dw = wave;  // index among the loading waves
     const int rowA0 = dw * NIA * (64 / CPRA) + lane / CPRA, rowB0 = dw * NIB * (64 / CPRB) + lane / CPRB;
-    const int voffA = rowA0 * rowA + (((lane % CPRA) ^ swz_key<RBA>(rowA0)) << 4);
-    const int voffB = rowB0 * rowB + (((lane % CPRB) ^ swz_key<RBB>(rowB0)) << 4);
-    const int voffA1 = RBA == 128 ? (voffA ^ 64) : voffA, voffB1 = RBB == 128 ? (voffB ^ 64) : voffB;
+    const int keyA = swz_key<RBA>(rowA0), keyB = swz_key<RBB>(rowB0);
+    const int keyA1 = RBA == 128 ? (keyA ^ 4) : keyA, keyB1 = RBB == 128 ? (keyB ^ 4) : keyB;
+    const int voffA = rowA0 * rowA + (((lane % CPRA) ^ keyA) << 4);
+    const int voffB = rowB0 * rowB + (((lane % CPRB) ^ keyB) << 4);
+    const int voffA1 = rowA0 * rowA + (((lane % CPRA) ^ keyA1) << 4);
+    const int voffB1 = rowB0 * rowB + (((lane % CPRB) ^ keyB1) << 4);
 
     // scale slot loads: eight 64-row instructions (four for A's rows, four
     // for B's), NSI per loading wave; 16 bytes of each row, one line per row
     constexpr int NSI = 8 / NWD;
     const int sop = (dw * NSI) >> 2;
     const int srow0 = ((dw * NSI) & 3) * 64;
-    const int svoff = (srow0 + lane) * kblocks;
+    const int sstride = sop ? srowB : srowA;  // uniform: the operand this wave loads
+    const int svoff = (srow0 + lane) * sstride;
 
     // codes of stage kt into code buffer S; with SCALES, also the scales of
     // stages kt .. kt + SPS - 1 into scale slot T.  Past the last stage the
@@ -754,7 +765,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
         if constexpr (decltype(SCALES)::value) {
 #pragma unroll
             for (int u = 0; u < NSI; u++)
-                dma16(sop ? rSB : rSA, stS(T, sop) + (srow0 + 64 * u) * 16, svoff + 64 * u * kblocks,
+                dma16(sop ? rSB : rSA, stS(T, sop) + (srow0 + 64 * u) * 16, svoff + 64 * u * sstride,
                       live ? pk * SBY : (int)(sop ? nrecSB : nrecSA));
         }
     };
@@ -1082,12 +1093,14 @@ hipError_t launch_fmt(const GemmArgs &g, bool bf16, hipStream_t stream) {
     const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(NT);
     constexpr bool fp4 = FA == E2M1 && FB == E2M1;
     // pipelined kernels: K a whole number of scale slots (16 scale bytes =
-    // 512 elements per row), 16-byte aligned codes, dword-aligned scale rows,
-    // offsets in 32 bits
-    const int64_t rowA = FA == E2M1 ? g.K / 2 : g.K, rowB = FB == E2M1 ? g.K / 2 : g.K;
+    // 512 elements per row), code and scale row strides multiples of 16 bytes
+    // (as the dense ones are then), 16-byte aligned code and dword-aligned
+    // scale pointers, offsets in 32 bits
+    const int64_t ldmax = g.lda > g.ldb ? g.lda : g.ldb, ldsmax = g.ldsa > g.ldsb ? g.ldsa : g.ldsb;
     const bool pipelined = g.K % 512 == 0 && ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.b % 16 == 0) &&
                            ((uintptr_t)g.as % 4 == 0) && ((uintptr_t)g.bs % 4 == 0) &&
-                           (int64_t)BM * (rowA > rowB ? rowA : rowB) < ((int64_t)1 << 31);
+                           g.lda % 16 == 0 && g.ldb % 16 == 0 && g.ldsa % 16 == 0 && g.ldsb % 16 == 0 &&
+                           (int64_t)BM * ldmax < ((int64_t)1 << 31) && (int64_t)BM * ldsmax < ((int64_t)1 << 31);
     if (pipelined) {
         const dim3 block(pipe::PNT);
         if constexpr (fp4) {

@@ -61,9 +61,15 @@ struct QuantJob {
 hipError_t launch_quantize_pair(int mode, int fmt, uint32_t sign_mask, const QuantJob &a, const QuantJob &b,
                                 hipStream_t stream);
 
-// GEMM launcher (mx_gemm.hip).
-hipError_t launch_gemm(const uint8_t *a, const uint8_t *as, int fa, const uint8_t *b,
-                       const uint8_t *bs, int fb, int64_t M, int64_t N, int64_t K, void *c,
+// GEMM launcher (mx_gemm.hip); operand row strides in bytes (codes, scales).
+hipError_t launch_gemm(const uint8_t *a, int64_t lda, const uint8_t *as, int64_t ldsa, int fa, const uint8_t *b,
+                       int64_t ldb, const uint8_t *bs, int64_t ldsb, int fb, int64_t M, int64_t N, int64_t K, void *c,
                        bool bf16_out, int64_t ldc, hipStream_t stream);
+
+// Row mode with strided outputs: row r's codes at codes + r * ld_codes, its
+// scales at scales + r * ld_scales (bytes).
+hipError_t launch_quantize_rows_strided(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                        uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                                        hipStream_t stream);
 
 }  // namespace mx

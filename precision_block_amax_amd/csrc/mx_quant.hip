@@ -51,6 +51,29 @@ hipError_t launch_rows_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_
     return hipGetLastError();
 }
 
+// strided outputs (OSTR): the row index comes from the octet index in both
+// input layouts, so only the non-contiguous input variants are instantiated
+template <int F>
+hipError_t launch_rows_strided_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint8_t *codes,
+                                   int64_t ld_codes, uint8_t *scales, int64_t ld_scales, hipStream_t stream) {
+    const uint64_t total = (uint64_t)rows * (uint64_t)cols / 8;
+    const uint32_t opr = (uint32_t)(cols / 8);
+    constexpr int CB = F == E2M1 ? 4 : 8;
+    const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0) && ((uintptr_t)codes % CB == 0) && (ld_codes % CB == 0);
+    const uint32_t per_block = kRowThreads * kRowUnroll;
+    const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+    const FastDiv div(opr);
+    if (vec)
+        hipLaunchKernelGGL((k_quantize_rows<F, false, true, false, true>), grid, dim3(kRowThreads), 0, stream, x, ldx,
+                           (uint32_t)total, opr, div, codes, scales, nullptr, 0, 0u, 0u, FastDiv(), nullptr, nullptr,
+                           0u, ld_codes, ld_scales);
+    else
+        hipLaunchKernelGGL((k_quantize_rows<F, false, false, false, true>), grid, dim3(kRowThreads), 0, stream, x, ldx,
+                           (uint32_t)total, opr, div, codes, scales, nullptr, 0, 0u, 0u, FastDiv(), nullptr, nullptr,
+                           0u, ld_codes, ld_scales);
+    return hipGetLastError();
+}
+
 template <int F, bool ROTATE>
 hipError_t launch_tr_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint32_t mask,
                          uint8_t *codes, uint8_t *scales, hipStream_t stream) {
@@ -148,6 +171,16 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, i
     case E4M3: return launch_rows_fmt<E4M3>(x, rows, cols, ldx, codes, scales, stream);
     case E5M2: return launch_rows_fmt<E5M2>(x, rows, cols, ldx, codes, scales, stream);
     default: return launch_rows_fmt<E2M1>(x, rows, cols, ldx, codes, scales, stream);
+    }
+}
+
+hipError_t launch_quantize_rows_strided(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                        uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                                        hipStream_t stream) {
+    switch (fmt) {
+    case E4M3: return launch_rows_strided_fmt<E4M3>(x, rows, cols, ldx, codes, ld_codes, scales, ld_scales, stream);
+    case E5M2: return launch_rows_strided_fmt<E5M2>(x, rows, cols, ldx, codes, ld_codes, scales, ld_scales, stream);
+    default: return launch_rows_strided_fmt<E2M1>(x, rows, cols, ldx, codes, ld_codes, scales, ld_scales, stream);
     }
 }
 

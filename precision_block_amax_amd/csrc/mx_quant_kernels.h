@@ -90,14 +90,16 @@ __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d 
 // Row mode.  Octet o covers elements 8o .. 8o+7 of the row-major [rows x cols]
 // view; cols % 32 == 0 keeps every block inside one quad of lanes.  With
 // PAIR, workgroups from `split` on quantize a second tensor (x1 ...), so that
-// both operands of a GEMM take one launch.
-template <int F, bool CONTIG, bool VEC, bool PAIR = false>
+// both operands of a GEMM take one launch.  With OSTR, row r's codes start at
+// codes + r * ldco and its scales at scales + r * ldsc (bytes), e.g. rows of
+// [codes | scales] in one buffer.
+template <int F, bool CONTIG, bool VEC, bool PAIR = false, bool OSTR = false>
 __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
     const uint16_t *__restrict__ x, int64_t ldx, uint32_t total_oct, uint32_t oct_per_row,
     FastDiv row_div, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
     const uint16_t *__restrict__ x1 = nullptr, int64_t ldx1 = 0, uint32_t total_oct1 = 0,
     uint32_t oct_per_row1 = 0, FastDiv row_div1 = FastDiv(), uint8_t *__restrict__ codes1 = nullptr,
-    uint8_t *__restrict__ scales1 = nullptr, uint32_t split = 0) {
+    uint8_t *__restrict__ scales1 = nullptr, uint32_t split = 0, int64_t ldco = 0, int64_t ldsc = 0) {
     uint32_t blk = blockIdx.x;
     if (PAIR && blk >= split) {  // uniform across the workgroup
         blk -= split;
@@ -154,25 +156,35 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
             hi = finite ? hi : 0u;
         }
         if (o < total_oct) {
+            constexpr int CB = F == E2M1 ? 4 : 8;  // code bytes per octet
+            uint8_t *cp, *sp;
+            if (OSTR) {
+                const uint32_t r = row_div.div(o), c = o - r * oct_per_row;
+                cp = codes + (int64_t)r * ldco + (uint64_t)c * CB;
+                sp = scales + (int64_t)r * ldsc + (c >> 2);
+            } else {
+                cp = codes + (uint64_t)o * CB;
+                sp = scales + (o >> 2);
+            }
             if (F == E2M1) {
                 if (VEC) {
-                    *reinterpret_cast<uint32_t *>(codes + (uint64_t)o * 4) = packed;
+                    *reinterpret_cast<uint32_t *>(cp) = packed;
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 4; i++) codes[(uint64_t)o * 4 + i] = (uint8_t)(packed >> (8 * i));
+                    for (int i = 0; i < 4; i++) cp[i] = (uint8_t)(packed >> (8 * i));
                 }
             } else {
                 if (VEC) {
-                    *reinterpret_cast<uint2 *>(codes + (uint64_t)o * 8) = make_uint2(lo, hi);
+                    *reinterpret_cast<uint2 *>(cp) = make_uint2(lo, hi);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
-                        codes[(uint64_t)o * 8 + i] = (uint8_t)(lo >> (8 * i));
-                        codes[(uint64_t)o * 8 + 4 + i] = (uint8_t)(hi >> (8 * i));
+                        cp[i] = (uint8_t)(lo >> (8 * i));
+                        cp[4 + i] = (uint8_t)(hi >> (8 * i));
                     }
                 }
             }
-            if ((threadIdx.x & 3u) == 0) scales[o >> 2] = (uint8_t)(finite ? e + 127 : 0xFF);
+            if ((threadIdx.x & 3u) == 0) *sp = (uint8_t)(finite ? e + 127 : 0xFF);
         }
     }
 }

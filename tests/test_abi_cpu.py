@@ -28,6 +28,8 @@ def L():
     lib.mx_quantize_transpose_sr.argtypes = [P, i64, i64, i64, i32, u32, ctypes.c_uint64, i32, P, P, P]
     lib.mx_quantize_pair.argtypes = [i32, i32, u32, P, i64, i64, i64, P, P, P, i64, i64, i64, P, P, P]
     lib.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
+    lib.mx_quantize_strided.argtypes = [P, i64, i64, i64, i32, P, i64, P, i64, P]
+    lib.mx_gemm_strided.argtypes = [P, i64, P, i64, i32, P, i64, P, i64, i32, i64, i64, i64, P, i32, i64, P]
     lib.mx_status_string.argtypes = [ctypes.c_int]
     lib.mx_status_string.restype = ctypes.c_char_p
     return lib
@@ -41,8 +43,8 @@ def declared_functions():
 def test_exports_every_declared_function(L):
     names = declared_functions()
     assert {"mx_quantize", "mx_quantize_transpose", "mx_hadamard32_quantize", "mx_quantize_dual",
-            "mx_quantize_transpose_sr", "mx_quantize_pair", "mx_gemm", "mx_status_string",
-            "mx_version"} <= set(names)
+            "mx_quantize_transpose_sr", "mx_quantize_pair", "mx_gemm", "mx_quantize_strided",
+            "mx_gemm_strided", "mx_status_string", "mx_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), "libmx.so does not export %s" % n
 
@@ -144,6 +146,45 @@ def test_gemm_rejects(L):
     assert f(None, AS, E4M3, B, BS, E4M3, 64, 64, 64, Cc, 0, 64, None) == INVALID
     assert f(A, AS, E4M3, B, BS, E4M3, 64, 64, 64, P(0x10000100), 0, 64, None) == INVALID  # C overlaps A
     assert f(None, None, E4M3, None, None, E4M3, 0, 64, 64, None, 0, 64, None) == OK       # empty
+
+
+def test_quantize_strided_rejects(L):
+    f = L.mx_quantize_strided
+    # a payload of 64 rows x 4096 E4M3 elements: rows of [4096 code bytes | 128 scale bytes]
+    PL = P(0x20000000)
+    ok = lambda **k: [k.get("x", X), k.get("rows", 64), k.get("cols", 4096), k.get("ldx", 4096), k.get("fmt", E4M3),
+                      k.get("c", PL), k.get("ldc", 4224), k.get("s", P(0x20000000 + 4096)), k.get("lds", 4224), None]
+    assert f(*ok(cols=4008, ldx=4008)) == INVALID          # cols % 32
+    assert f(*ok(ldc=4095)) == INVALID                     # code rows overlap each other
+    assert f(*ok(lds=127)) == INVALID                      # scale row stride below cols / 32
+    assert f(*ok(s=P(0x20000000 + 4000))) == INVALID       # scales inside the codes of their row
+    assert f(*ok(s=P(0x20000000 + 4100))) == INVALID       # scales run into the next row's codes
+    assert f(*ok(lds=4096 + 256)) == INVALID               # interleaved with a different stride
+    assert f(*ok(x=P(0x20000100))) == INVALID              # input over the payload
+    assert f(*ok(fmt=4)) == INVALID
+    assert f(*ok(c=None)) == INVALID
+    assert f(*ok(ldx=4095)) == INVALID
+    assert f(*ok(rows=0, x=None, c=None, s=None)) == OK    # empty
+    # E2M1 payload rows: 2048 code bytes + 128 scale bytes; misplaced scales are rejected
+    assert f(*ok(fmt=E2M1, ldc=2176, lds=2176, s=P(0x20000000 + 2047))) == INVALID
+
+
+def test_gemm_strided_rejects(L):
+    f = L.mx_gemm_strided
+    A, AS, B, BS, Cc = (P(a) for a in (0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000))
+    args = lambda **k: [k.get("a", A), k.get("lda", 512), k.get("as_", AS), k.get("ldsa", 16), E4M3,
+                        k.get("b", B), k.get("ldb", 512), k.get("bs", BS), k.get("ldsb", 16), k.get("fb", E2M1),
+                        k.get("M", 64), k.get("N", 64), k.get("K", 512), k.get("c", Cc), 0, k.get("ldc", 64), None]
+    assert f(*args(lda=511)) == INVALID                  # code row stride below K bytes (E4M3)
+    assert f(*args(lda=520)) == INVALID                  # code row stride not a multiple of 16
+    assert f(*args(ldb=255)) == INVALID                  # below K / 2 (E2M1)
+    assert f(*args(ldsa=15)) == INVALID                  # scale row stride below K / 32
+    assert f(*args(ldsb=15)) == INVALID
+    assert f(*args(K=500)) == INVALID
+    assert f(*args(ldc=63)) == INVALID
+    assert f(*args(c=P(0x10000000 + 63 * 512))) == INVALID   # C over A's last row (strided extent)
+    assert f(*args(c=P(0x20000000 + 63 * 16))) == INVALID    # C over A's last scale row
+    assert f(*args(M=0, a=None, as_=None, c=None)) == OK     # empty
 
 
 def test_valid_call_without_a_device_reports_hip_error(L):
