@@ -44,15 +44,15 @@ CONFIGS = (1, 2, 3)  # the three Llama-3.1-8B workloads
 WORKLOAD = "llama31_8b_linear_set"
 PROFILE_COMMANDS = (
     "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/prof_trace -o trace -- "
-    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra --iso-reps 5",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/prof_fetch -o fetch -- "
-    "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
+    "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-extra --iso-reps 5 --calibrate-copy",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/prof_write -o write -- "
-    "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy",
+    "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-extra --iso-reps 5 --calibrate-copy",
     "rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d rocprof_out/prof_clock -o clock -- "
-    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra --iso-reps 5",
     "rocprofv3 --pmc MfmaUtil --output-format csv -d rocprof_out/prof_mfma -o mfma -- "
-    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra --iso-reps 5",
 )
 XCDS = 8          # MI355X: GRBM_GUI_ACTIVE sums the busy cycles of the 8 accelerator dies
 PEAK_SCLK_GHZ = 2.4
@@ -62,6 +62,11 @@ MIN_CLOCK_US = 100  # shortest kernel whose counted busy cycles give a clock
 def quant_bytes(rows: int, cols: int, fmt: str) -> float:
     """algorithmic HBM bytes of one quantize call: bf16 in, codes + scales out"""
     return rows * cols * (2.0 + (0.5 if fmt == "e2m1" else 1.0) + 1.0 / 32)
+
+
+def spread(samples) -> list:
+    """10th and 90th percentile of a list of times"""
+    return [round(float(np.percentile(samples, 10)), 4), round(float(np.percentile(samples, 90)), 4)]
 
 
 def kernel_source_sha() -> str:
@@ -171,16 +176,31 @@ class Step:
                 ev[1].record()
 
 
-def cpu_baseline(seed: int, step_flops: float) -> dict:
+def cpu_model() -> str:
+    """the host CPU's model name"""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(seed: int, step_flops: float, launches=None, kernels=None) -> dict:
     """the oracle on a bounded sample of the same step, extrapolated to the
-    step; rows per quantize and rows of A per GEMM are sampled"""
+    step; rows per quantize and rows of A per GEMM are sampled.  Per kernel:
+    the oracle's extrapolated time and rate, and the GPU kernel's speed-up
+    over it (in-step GPU time)."""
     import oracle
-    qrows, grow_a, grow_b = 512, 8, 40
+    # GEMM rows 128 and 512: enough that the fp64 product, not the operands' dequantization, sets the slope
+    qrows, grow_a, grow_b = 512, 128, 512
     t_total = 0.0
-    parts = []
+    parts, part_s, per_kernel = [], {}, []
     for ci in CONFIGS:
         cfg = workloads.config(ci)
-        ops = {}
         for q in cfg.quants:
             spec = cfg.tensor(q.tensor)
             x = workloads.draw_tensor(cfg, q.tensor, seed=seed, rows=(0, qrows))
@@ -190,8 +210,12 @@ def cpu_baseline(seed: int, step_flops: float) -> dict:
             t0 = time.perf_counter()
             fn()
             dt = time.perf_counter() - t0
-            t_total += dt * spec.rows / qrows
+            t_full = dt * spec.rows / qrows
+            t_total += t_full
+            part_s[(cfg.name, q.name)] = t_full
             parts.append("%s/%s: %d of %d rows" % (cfg.name, q.name, qrows, spec.rows))
+            per_kernel.append({"kernel": "%s/%s %s %s" % (cfg.name, q.name, q.kind, q.fmt), "oracle_s": round(t_full, 4),
+                               "oracle_GBps": round(quant_bytes(spec.rows, spec.cols, q.fmt) / t_full / 1e9, 3)})
         for gm in cfg.gemms:
             qa, qb = cfg.quant(gm.a), cfg.quant(gm.b)
             # operands from the oracle's own quantizers (full tensors: the GEMM needs all of B)
@@ -210,14 +234,222 @@ def cpu_baseline(seed: int, step_flops: float) -> dict:
                 times.append(time.perf_counter() - t0)
             per_row = max(times[1] - times[0], 0.0) / (grow_b - grow_a)
             fixed = max(times[0] - per_row * grow_a, 0.0)
-            t_total += fixed + per_row * gm.M
+            t_g = fixed + per_row * gm.M
+            t_total += t_g
+            part_s[(cfg.name, gm.name)] = t_g
             parts.append("%s/%s: GEMM rows %d and %d of %d, linear fit" % (cfg.name, gm.name, grow_a, grow_b, gm.M))
+            per_kernel.append({"kernel": "%s/%s gemm %dx%dx%d" % (cfg.name, gm.name, gm.M, gm.N, gm.K),
+                               "oracle_s": round(t_g, 3),
+                               "oracle_GFLOPs": round(2.0 * gm.M * gm.N * gm.K / t_g / 1e9, 2)})
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         cores = os.cpu_count() or 1
+    speedups = []
+    if launches is not None and kernels is not None:
+        # each GPU launch against the oracle time of the quantize calls or GEMM it performs
+        for (name, _, _, _), k in zip(launches, kernels):
+            cfg_name, rest = name.split("/", 1)
+            names = rest.split()[0].split("+")
+            t = sum(part_s.get((cfg_name, nm), 0.0) for nm in names)
+            if t > 0:
+                speedups.append({"kernel": name, "oracle_s": round(t, 4), "gpu_ms": round(k["ms"], 4),
+                                 "gpu_over_oracle": round(t / (k["ms"] * 1e-3), 1)})
     return {"value": step_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "; ".join(parts) + "; per-step time extrapolated to %.1f s" % t_total}
+            "cpu_model": cpu_model(),
+            "sample": "; ".join(parts) + "; per-step time extrapolated to %.1f s" % t_total,
+            "kernels": per_kernel, "gpu_over_oracle": speedups}
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _time_sequence(torch, launches, reps):
+    """median over `reps` passes of each launch's event time and of the whole pass
+    (launches run back to back on the current stream; no cache flush in between)"""
+    per = [[] for _ in launches]
+    whole = []
+    for _ in range(reps):
+        evs = [_events(torch) for _ in launches]
+        w0, w1 = _events(torch)
+        w0.record()
+        for (_, fn), e in zip(launches, evs):
+            e[0].record()
+            fn()
+            e[1].record()
+        w1.record()
+        torch.cuda.synchronize()
+        for k, e in enumerate(evs):
+            per[k].append(e[0].elapsed_time(e[1]))
+        whole.append(w0.elapsed_time(w1))
+    seq = []
+    for _ in range(reps):  # the same pass without per-launch events, for the pass time alone
+        w0, w1 = _events(torch)
+        w0.record()
+        for _, fn in launches:
+            fn()
+        w1.record()
+        torch.cuda.synchronize()
+        seq.append(w0.elapsed_time(w1))
+    return [float(np.median(p)) for p in per], float(np.median(seq))
+
+
+def linear_layer(mx, torch, seed: int, reps: int) -> dict:
+    """One whole Llama-3.1-8B gate+up linear layer in the MXFP4 recipe (FP4-training
+    article on hzrcw.cc, section 02): X, W and dY each quantized once by the
+    dual-direction quantizer (row form + transposed or rotated form from one read),
+    then Fprop, Dgrad and Wgrad.  The same layer with the six single-direction
+    quantize calls is timed beside it; the difference is what the fused quantizer
+    saves where it applies.  Passes run back to back (median of `reps`)."""
+    cfg = workloads.config(5)
+    dev = {t.name: torch.from_numpy(workloads.draw_tensor(cfg, t.name, seed=seed).view(np.int16)).view(
+        torch.bfloat16).to("cuda") for t in cfg.tensors}
+    ops = {}
+    for q in cfg.quants:
+        x = dev[q.tensor]
+        rows, k = (x.shape[0], x.shape[1]) if q.kind == "row" else (x.shape[1], x.shape[0])
+        ops[q.name] = (torch.empty((rows, mx.code_cols(k, q.fmt)), dtype=torch.uint8, device="cuda"),
+                       torch.empty((rows, k // 32), dtype=torch.uint8, device="cuda"), q.fmt)
+    outs = {g.name: torch.empty((g.M, g.N), dtype=torch.bfloat16 if g.out == "bf16" else torch.float32,
+                                device="cuda") for g in cfg.gemms}
+
+    def gemm_launch(g):
+        a, b = ops[g.a], ops[g.b]
+        return ("%s %dx%dx%d %sx%s" % (g.name, g.M, g.N, g.K, a[2], b[2]),
+                lambda: mx.gemm(a[0], a[1], a[2], b[0], b[1], b[2], out_dtype=outs[g.name].dtype, out=outs[g.name]))
+
+    duals, singles, work = [], [], {}
+    for src, q_row, q_t in workloads.LAYER_DUALS:
+        qr, qt = cfg.quant(q_row), cfg.quant(q_t)
+        x = dev[src]
+        rot = qt.kind == "hadamard"
+        o = ops[q_row][:2] + ops[q_t][:2]
+        name = "dual %s %dx%d: %s row + %s %s" % (src, x.shape[0], x.shape[1], qr.fmt, qt.fmt,
+                                                   "rotated" if rot else "transposed")
+        duals.append((name, lambda x=x, qr=qr, qt=qt, rot=rot, o=o: mx.quantize_dual(
+            x, qr.fmt, qt.fmt, rot, 0, out=o)))
+        n_el = x.numel()
+        work[name] = n_el * (2.0 + (0.5 if qr.fmt == "e2m1" else 1.0) + (0.5 if qt.fmt == "e2m1" else 1.0) + 2 / 32)
+        for q in (qr, qt):
+            c, sc, _ = ops[q.name]
+            fn = {"row": lambda x=x, q=q, c=c, sc=sc: mx.quantize(x, q.fmt, out=(c, sc)),
+                  "transpose": lambda x=x, q=q, c=c, sc=sc: mx.quantize_transpose(x, q.fmt, out=(c, sc)),
+                  "hadamard": lambda x=x, q=q, c=c, sc=sc: mx.hadamard32_quantize(x, q.fmt, 0, out=(c, sc))}[q.kind]
+            nm = "%s %s %s" % (q.name, q.kind, q.fmt)
+            singles.append((nm, fn))
+            work[nm] = quant_bytes(x.shape[0], x.shape[1], q.fmt)
+    gemms = [gemm_launch(g) for g in cfg.gemms]
+    for g, (nm, _) in zip(cfg.gemms, gemms):
+        work[nm] = 2.0 * g.M * g.N * g.K
+    for _ in range(2):  # warm-up
+        for _, fn in duals + singles + gemms:
+            fn()
+    torch.cuda.synchronize()
+    t_dual, layer_dual = _time_sequence(torch, duals + gemms, reps)
+    t_single, layer_single = _time_sequence(torch, singles + gemms, reps)
+    flops = sum(2.0 * g.M * g.N * g.K for g in cfg.gemms)
+
+    def row(name, ms):
+        w = work[name]
+        if name.startswith(("fprop", "dgrad", "wgrad")):
+            tf = w / (ms * 1e-3) / 1e12
+            return {"launch": name, "ms": round(ms, 4), "TFLOPs": round(tf, 1), "frac_of_fp4_peak": round(
+                tf / PEAK_TFLOPS["fp4"], 4)}
+        gb = w / (ms * 1e-3) / 1e9
+        return {"launch": name, "ms": round(ms, 4), "GBps": round(gb, 1), "frac_of_hbm_peak": round(gb / PEAK_HBM_GBPS, 4)}
+
+    return {
+        "layer": "Llama-3.1-8B gate+up: X [8192x4096], W [28672x4096], dY [8192x28672]; MXFP4 Fprop, Dgrad, "
+                 "rotated Wgrad",
+        "layer_ms_dual_quantize": round(layer_dual, 4), "layer_ms_single_quantizes": round(layer_single, 4),
+        "layer_TFLOPs_dual": round(flops / (layer_dual * 1e-3) / 1e12, 1),
+        "quantize_ms_dual": round(sum(t_dual[:len(duals)]), 4),
+        "quantize_ms_single": round(sum(t_single[:len(singles)]), 4),
+        "launches_dual": [row(n, t) for (n, _), t in zip(duals + gemms, t_dual)],
+        "launches_single": [row(n, t) for (n, _), t in zip(singles, t_single)],
+        "how": "median of %d back-to-back passes; per-launch figures from event pairs around each launch, "
+               "pass times from passes without them" % reps,
+    }
+
+
+def _device_tensor(torch, spec, gen):
+    """a bf16 tensor of the recipe's shape and distribution drawn on the device
+    (timing input only: the 70B set's host-seeded bytes would take the host
+    minutes to draw)"""
+    out = torch.empty((spec.rows, spec.cols), dtype=torch.bfloat16, device="cuda")
+    chan = None
+    if spec.outlier_channels > 0:
+        n_out = int(round(spec.outlier_channels * spec.cols))
+        chan = torch.randperm(spec.cols, generator=gen, device="cuda")[:n_out]
+    for r0 in range(0, spec.rows, 2048):
+        r1 = min(spec.rows, r0 + 2048)
+        shape = (r1 - r0, spec.cols)
+        v = torch.randn(shape, generator=gen, device="cuda")
+        if spec.dist == "t3":  # Student-t, 3 degrees of freedom: z / sqrt(chi2_3 / 3)
+            chi = sum(torch.randn(shape, generator=gen, device="cuda") ** 2 for _ in range(3))
+            v = v / torch.sqrt(chi / 3.0)
+        v *= spec.scale
+        if chan is not None:
+            v[:, chan] *= spec.outlier_factor
+        out[r0:r1] = v.to(torch.bfloat16)
+    return out
+
+
+def llama70b_set(mx, torch, seed: int, reps: int = 3) -> dict:
+    """The Llama-3.1-70B single-layer linear set at 8192 tokens: each GEMM's two
+    quantize calls and the GEMM, back to back, per launch (median of `reps`
+    passes).  Eight of the nine GEMMs have FP8 operands and run on the bf16
+    carrier; they are reported against the bf16 matrix peak it runs on and
+    against MXFP8's."""
+    cfg = workloads.config(4)
+    gen = torch.Generator(device="cuda").manual_seed(seed + 70)
+    dev = {t.name: _device_tensor(torch, t, gen) for t in cfg.tensors}
+    out, total_ms, total_flops, quant_ms, quant_bytes_ = [], 0.0, 0.0, 0.0, 0.0
+    for g in cfg.gemms:
+        launches, ops = [], {}
+        for qn in (g.a, g.b):
+            q = cfg.quant(qn)
+            x = dev[q.tensor]
+            rows, k = (x.shape[0], x.shape[1]) if q.kind == "row" else (x.shape[1], x.shape[0])
+            c = torch.empty((rows, mx.code_cols(k, q.fmt)), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((rows, k // 32), dtype=torch.uint8, device="cuda")
+            ops[qn] = (c, sc, q.fmt)
+            fn = {"row": lambda x=x, q=q, c=c, sc=sc: mx.quantize(x, q.fmt, out=(c, sc)),
+                  "transpose": lambda x=x, q=q, c=c, sc=sc: mx.quantize_transpose(x, q.fmt, out=(c, sc)),
+                  "hadamard": lambda x=x, q=q, c=c, sc=sc: mx.hadamard32_quantize(x, q.fmt, 0, out=(c, sc))}[q.kind]
+            launches.append(("%s %s %s" % (qn, q.kind, q.fmt), fn, quant_bytes(x.shape[0], x.shape[1], q.fmt)))
+        a, b = ops[g.a], ops[g.b]
+        cbuf = torch.empty((g.M, g.N), dtype=torch.bfloat16 if g.out == "bf16" else torch.float32, device="cuda")
+        launches.append(("%s gemm" % g.name, lambda a=a, b=b, cbuf=cbuf: mx.gemm(
+            a[0], a[1], a[2], b[0], b[1], b[2], out_dtype=cbuf.dtype, out=cbuf), 2.0 * g.M * g.N * g.K))
+        for _, fn, _ in launches:
+            fn()
+        torch.cuda.synchronize()
+        t, _ = _time_sequence(torch, [(n, fn) for n, fn, _ in launches], reps)
+        arith = "fp4" if a[2] == "e2m1" and b[2] == "e2m1" else "bf16"
+        tf = launches[2][2] / (t[2] * 1e-3) / 1e12
+        r = {"gemm": g.name, "M": g.M, "N": g.N, "K": g.K, "formats": "%sx%s" % (a[2], b[2]), "ms": round(t[2], 4),
+             "TFLOPs": round(tf, 1), "arith": arith, "frac": round(tf / PEAK_TFLOPS[arith], 4),
+             "quantize": [{"call": launches[k][0], "ms": round(t[k], 4),
+                           "GBps": round(launches[k][2] / (t[k] * 1e-3) / 1e9, 1),
+                           "frac_of_hbm_peak": round(launches[k][2] / (t[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+                          for k in (0, 1)]}
+        if arith == "bf16":
+            r["frac_of_mxfp8_peak"] = round(tf / PEAK_TFLOPS["fp8"], 4)
+        out.append(r)
+        total_ms += t[2]
+        total_flops += launches[2][2]
+        quant_ms += t[0] + t[1]
+        quant_bytes_ += launches[0][2] + launches[1][2]
+        del launches, ops, cbuf, a, b
+    return {"gemms": out, "gemm_ms_total": round(total_ms, 3),
+            "gemm_TFLOPs_aggregate": round(total_flops / (total_ms * 1e-3) / 1e12, 1),
+            "quantize_ms_total": round(quant_ms, 3),
+            "quantize_GBps_aggregate": round(quant_bytes_ / (quant_ms * 1e-3) / 1e9, 1),
+            "inputs": "drawn on the device with the recipe's shapes and distributions (timing only; the parity "
+                      "tests use the seeded host draws)",
+            "how": "each GEMM after its two quantize calls, back to back; median of %d passes" % reps}
 
 
 def _read_csv(path):
@@ -302,9 +534,10 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
         if "mx::" in r["Kernel_Name"] and (first_flush is None or int(r["Dispatch_Id"]) < first_flush):
             step_calls.setdefault(r["Kernel_Name"], []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines += ["", "Inside the timed steps only (each kernel's last %d launches before the first cache "
-              "fill: bench.py runs %d warm-up steps, %d steps with every launch bracketed by events, "
-              "then the %d timed steps):" % (steps, warmup, steps, steps), "",
+    lines += ["", "Inside the steps only (each kernel's last %d launches before the first cache fill: "
+              "bench.py runs %d warm-up steps, %d steps per launch with events around that launch alone, "
+              "the %d timed steps, then %d steps each bracketed by one event pair, whose launches these "
+              "are):" % (steps, warmup, steps, steps, steps), "",
               "| kernel | timed calls | average (us) |", "|---|---|---|"]
     for k, d in sorted(step_calls.items(), key=lambda kv: -sum(kv[1])):
         timed = d[-steps:]
@@ -473,10 +706,13 @@ def kernel_symbol(name: str) -> str:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=workloads.DEFAULT_SEED)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="leave out the whole-layer and Llama-3.1-70B sections (profiling runs)")
+    ap.add_argument("--iso-reps", type=int, default=50, help="lone launches per kernel (median)")
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table to stderr")
     ap.add_argument("--ablation", action="store_true",
                     help="only the weight-gradient rotation ablation (dW error of the Wgrad recipes)")
@@ -517,54 +753,52 @@ def main() -> int:
         step.run()
     torch.cuda.synchronize()
 
-    # Per-kernel times inside the step: `steps` instrumented steps with every launch bracketed
-    # by HIP events on the stream it runs on (torch's current stream, which the binding passes
-    # to the library).  They name the dominant kernel; the timed steps then bracket that
-    # kernel alone, so that the other launches' events (30-70 us per step) stay out of the
-    # measured step time.
+    # Per-kernel times inside the step: for each launch, `steps` steps in which HIP events
+    # (on the stream it runs on: torch's current stream, which the binding passes to the
+    # library) bracket that launch alone, so no other launch's events sit in the step.
+    # The median names the dominant kernel; the timed steps then bracket it alone.
     n = len(step.launches)
     new_ev = lambda: [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-    events = [[new_ev() for _ in range(n)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        step.run(events[s])
-    torch.cuda.synchronize()
-    in_step = [float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
-               for i in range(n)]
-    dom_i = int(np.argmax(in_step))
+    in_step = []
+    for i in range(n):
+        evs = [new_ev() for _ in range(args.steps)]
+        for s_ in range(args.steps):
+            step.run(only=(i, evs[s_]))
+        torch.cuda.synchronize()
+        in_step.append([e[0].elapsed_time(e[1]) for e in evs])
+    in_step_med = [float(np.median(t)) for t in in_step]
+    dom_i = int(np.argmax(in_step_med))
     dom_events = [new_ev() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step.run(only=(dom_i, dom_events[s]))
+    for s_ in range(args.steps):
+        step.run(only=(dom_i, dom_events[s_]))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dom_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dom_events]))
+    dom_t = [e[0].elapsed_time(e[1]) for e in dom_events]
+    dom_ms = float(np.mean(dom_t))
     print("bench: timed %d steps, %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
+    # the spread of single steps: `steps` more steps, each bracketed by one event pair
+    step_events = [new_ev() for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        step_events[s_][0].record()
+        step.run()
+        step_events[s_][1].record()
+    torch.cuda.synchronize()
+    step_t = np.array([e[0].elapsed_time(e[1]) for e in step_events])
 
     # Each kernel again on its own: the last-level cache (256 MB) is first
     # filled with clean lines by reading a 512 MiB buffer, so the kernel
     # neither finds its inputs cached nor pays for writing back dirty lines
     # left by the previous kernel (inside the step a quantizer that follows a
-    # GEMM does, which can halve its read rate).  Median of five.
+    # GEMM does, which can halve its read rate).  Median of `iso_reps` calls.
     flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
     sink = torch.empty(1, dtype=torch.int64, device="cuda")
-    isolated = []
-    for (_, _, _, fn) in step.launches:
-        ts = []
-        for _ in range(5):
-            sink.copy_(flush.view(torch.int64).sum().view(1))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        isolated.append(float(np.median(ts)))
 
-    def alone(fn):
+    def alone(fn, reps=args.iso_reps):
         ts = []
-        for _ in range(5):
+        for _ in range(reps):
             sink.copy_(flush.view(torch.int64).sum().view(1))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -573,6 +807,8 @@ def main() -> int:
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         return float(np.median(ts))
+
+    isolated = [alone(fn) for (_, _, _, fn) in step.launches]
 
     # The fused dual-direction quantizer (one read, row form + rotated
     # transposed form) on the down-projection output gradient, against the
@@ -609,22 +845,40 @@ def main() -> int:
     del dy, sr_out
 
     # One rank's share of an FSDP2 MXFP8 weight all-gather: quantize its slab
-    # of gate/up weight rows (1/8 of dim 0) to E4M3; the payload it
-    # contributes to the gather is codes + scales instead of bf16.
+    # of gate/up weight rows (1/8 of dim 0) to E4M3 into its gather-ready
+    # payload (rows of [codes | scales], mx_quantize_strided); the payload it
+    # contributes to the gather is 1.03 bytes per element instead of bf16's 2.
+    # The GEMM on the gathered payload (the whole weight, read in place through
+    # mx_gemm_strided) is timed against the same GEMM on dense operands.
     cfg2 = workloads.config(2)
     wfull = workloads.draw_tensor(cfg2, "W", seed=args.seed)
     slab_rows = wfull.shape[0] // 8
-    slab = torch.from_numpy(wfull[:slab_rows].view(np.int16)).view(torch.bfloat16).to("cuda")
+    wdev = torch.from_numpy(wfull.view(np.int16)).view(torch.bfloat16).to("cuda")
     del wfull
-    so = mx.quantize(slab, "e4m3")
-    t_slab = alone(lambda: mx.quantize(slab, "e4m3", out=so))
+    slab = wdev[:slab_rows]
+    payload = mx.fsdp_payload(slab, "e4m3")
+    t_slab = alone(lambda: mx.fsdp_payload(slab, "e4m3", out=payload))
+    K2 = slab.shape[1]
+    width = mx.payload_width(K2, "e4m3")
+    gathered = torch.cat([mx.fsdp_payload(wdev[r * slab_rows:(r + 1) * slab_rows], "e4m3") for r in range(8)])
+    pc, ps = mx.payload_views(gathered, K2, "e4m3")
+    qw_dense = mx.quantize(wdev, "e4m3")
+    xq = mx.quantize(torch.from_numpy(workloads.draw_tensor(cfg2, "X", seed=args.seed).view(np.int16)).view(
+        torch.bfloat16).to("cuda"), "e4m3")
+    yb = torch.empty((xq[0].shape[0], wdev.shape[0]), dtype=torch.bfloat16, device="cuda")
+    t_g_payload = alone(lambda: mx.gemm(xq[0], xq[1], "e4m3", pc, ps, "e4m3", out_dtype=torch.bfloat16, out=yb), 10)
+    t_g_dense = alone(lambda: mx.gemm(xq[0], xq[1], "e4m3", qw_dense[0], qw_dense[1], "e4m3",
+                                      out_dtype=torch.bfloat16, out=yb), 10)
     nb = slab.numel()
     fsdp_shard = {"slab": "%s/W rows 0..%d of %d (one of 8 ranks)" % (cfg2.name, slab_rows, slab_rows * 8),
-                  "format": "e4m3", "ms": round(t_slab, 4),
-                  "GBps": round(quant_bytes(slab_rows, slab.shape[1], "e4m3") / (t_slab * 1e-3) / 1e9, 1),
-                  "gather_bytes": nb * (1 + 1.0 / 32), "gather_bytes_bf16": nb * 2.0,
-                  "gather_ratio": round((1 + 1.0 / 32) / 2.0, 4)}
-    del slab, so
+                  "format": "e4m3", "layout": "rows of [codes %d B | scales %d B], stride %d B" % (
+                      K2, K2 // 32, width),
+                  "ms": round(t_slab, 4),
+                  "GBps": round(slab_rows * K2 * (2.0 + width / K2) / (t_slab * 1e-3) / 1e9, 1),
+                  "gather_bytes": slab_rows * width, "gather_bytes_bf16": nb * 2.0,
+                  "gather_ratio": round(width / (2.0 * K2), 4),
+                  "gemm_on_gathered_payload_ms": round(t_g_payload, 4), "gemm_on_dense_operands_ms": round(t_g_dense, 4)}
+    del slab, payload, gathered, pc, ps, qw_dense, xq, yb, wdev
 
     # The full MXFP4 recipe and the mixed-format GEMMs at the gate/up layer's
     # shapes, each alone with a clean cache: Dgrad in FP4 (dX = dY W through
@@ -680,6 +934,13 @@ def main() -> int:
         del src, dst
     del flush
 
+    extra = {}
+    if not args.no_extra:
+        print("bench: whole gate/up linear layer", file=sys.stderr, flush=True)
+        extra["llama31_8b_gateup_layer_mxfp4"] = linear_layer(mx, torch, args.seed, args.iso_reps)
+        print("bench: Llama-3.1-70B layer set", file=sys.stderr, flush=True)
+        extra["llama31_70b_layer_linear_set"] = llama70b_set(mx, torch, args.seed)
+
     if args.calibrate_copy:
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -689,18 +950,21 @@ def main() -> int:
 
     kernels = []
     for i, (name, kind, work, _) in enumerate(step.launches):
-        ms = dom_ms if i == dom_i else in_step[i]  # the dominant kernel: its events in the timed steps
+        # median of the kernel's in-step samples; the dominant kernel: its events in the timed steps
+        ms = float(np.median(dom_t)) if i == dom_i else in_step_med[i]
         iso = isolated[i]
         if kind == "quant":
             ach, iach = work / (ms * 1e-3) / 1e9, work / (iso * 1e-3) / 1e9
             kernels.append({"kernel": name, "ms": ms, "bound": "hbm", "achieved": ach, "unit": "GB/s",
                             "peak": PEAK_HBM_GBPS, "frac": ach / PEAK_HBM_GBPS, "work": work,
+                            "ms_p10_p90": spread(dom_t if i == dom_i else in_step[i]),
                             "isolated": {"ms": iso, "achieved": iach, "frac": iach / PEAK_HBM_GBPS}})
         else:
             arith = kind.split(":")[1]
             ach, iach = work / (ms * 1e-3) / 1e12, work / (iso * 1e-3) / 1e12
             k = {"kernel": name, "ms": ms, "bound": "mfma", "achieved": ach, "unit": "TFLOP/s",
                  "peak": PEAK_TFLOPS[arith], "frac": ach / PEAK_TFLOPS[arith], "arith": arith, "work": work,
+                 "ms_p10_p90": spread(dom_t if i == dom_i else in_step[i]),
                  "isolated": {"ms": iso, "achieved": iach, "frac": iach / PEAK_TFLOPS[arith]}}
             if arith == "bf16":  # MXFP8 operands carried as bf16: also against the MXFP8 peak
                 k["frac_of_mxfp8_peak"] = ach / PEAK_TFLOPS["fp8"]
@@ -708,12 +972,16 @@ def main() -> int:
 
     dom = kernels[dom_i]
     traffic = measured_traffic(kernel_symbol(dom["kernel"]))
-    roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3), "peak": dom["peak"],
-                "unit": dom["unit"], "frac": round(dom["frac"], 4), "traffic": traffic, "kernel": dom["kernel"]}
+    # achieved: the dominant kernel's algorithmic flops over its AVERAGE event duration in the timed steps
+    dom_ach = dom["work"] / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": dom["bound"], "achieved": round(dom_ach, 3), "peak": dom["peak"],
+                "unit": dom["unit"], "frac": round(dom_ach / dom["peak"], 4), "traffic": traffic, "kernel": dom["kernel"],
+                "launch_ms_mean": round(dom_ms, 4), "launch_ms_median": round(float(np.median(dom_t)), 4),
+                "timed_launches": len(dom_t)}
     sclk = measured_clock(kernel_symbol(dom["kernel"]))
     if sclk is not None:  # the profiled run's sustained clock: the peak the kernel could reach at it
         roofline["sclk_ghz"] = round(sclk, 3)
-        roofline["frac_of_clock_adjusted_peak"] = round(dom["frac"] * PEAK_SCLK_GHZ / sclk, 4)
+        roofline["frac_of_clock_adjusted_peak"] = round(roofline["frac"] * PEAK_SCLK_GHZ / sclk, 4)
     mfma_util = measured_mfma_util(kernel_symbol(dom["kernel"]))
     if mfma_util is not None:  # the profiled run's MFMA busy share of the SIMD cycles
         roofline["mfma_busy_pct"] = round(mfma_util, 1)
@@ -726,6 +994,10 @@ def main() -> int:
         "metric": "MX-GEMM TFLOPS & quantize GB/s at Llama-3.1-8B shapes, % of MI355X peak",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "step_ms": {"median": round(float(np.median(step_t)), 4), "p10": round(float(np.percentile(step_t, 10)), 4),
+                    "p90": round(float(np.percentile(step_t, 90)), 4), "min": round(float(step_t.min()), 4),
+                    "max": round(float(step_t.max()), 4), "steps": int(step_t.size),
+                    "how": "a further pass of `steps` steps, each bracketed by one event pair"},
         "dtype": "mxfp8/mxfp4 operands, fp32 accumulate", "data": "synthetic",
         "config": {"workload": WORKLOAD, "global_batch": 8192, "seq_len": 8192, "parallelism": "none",
                    "gemms": [k["kernel"] for k in kernels if k["bound"] == "mfma"]},
@@ -737,14 +1009,18 @@ def main() -> int:
         "stochastic_rounding": stochastic_rounding,
         "hbm_copy": hbm_copy,
         "mxfp4_recipe_and_mixed_gemms": recipe,
+        **extra,
         "quantize_frac_of_hbm_peak_isolated": round(quant_gbps_iso / PEAK_HBM_GBPS, 4),
         "kernels": [{kk: (round(v, 4) if isinstance(v, float) else
                           {a: round(b, 4) for a, b in v.items()} if isinstance(v, dict) else v)
                      for kk, v in k.items() if kk != "work"} for k in kernels],
+        "kernel_timing": ("ms: median over `steps` steps in which events bracket that launch alone (the dominant "
+                          "kernel: its events in the timed steps); isolated: median of %d lone launches, each "
+                          "after a clean fill of the last-level cache" % args.iso_reps),
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle on a bounded sample)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(args.seed, step.flops)
+        line["cpu_baseline"] = cpu_baseline(args.seed, step.flops, step.launches, kernels)
     if args.kernels:
         print("%-70s %21s %7s   %s" % ("kernel", "in the step", "", "alone, clean cache"), file=sys.stderr)
         for k in kernels:

@@ -179,7 +179,30 @@ CONFIGS: Tuple[Config, ...] = (
             GemmSpec("down_wgrad", "qdY_down_H", "qh_H", 8192, 28672, T, "f32"),
         ),
     ),
+    # One whole Llama-3.1-8B gate+up linear layer in the MXFP4 recipe (FP4-training
+    # article, section 02: forward, activation-gradient and weight-gradient GEMMs in
+    # MXFP4, the weight gradient's operands rotated): each source tensor is needed in
+    # two forms, which the dual-direction quantizer produces from one read --
+    # X: row (Fprop) + rotated (Wgrad); W: row (Fprop) + transposed (Dgrad);
+    # dY: row (Dgrad) + rotated (Wgrad).
+    Config(
+        5, "llama31_8b_gateup_layer_mxfp4",
+        (_act("X", T, 4096), _weight("W", 28672, 4096, 0.02), _grad("dY", T, 28672)),
+        (
+            QuantSpec("qX", "X", "row", E2M1), QuantSpec("qX_H", "X", "hadamard", E2M1),
+            QuantSpec("qW", "W", "row", E2M1), QuantSpec("qW_T", "W", "transpose", E2M1),
+            QuantSpec("qdY", "dY", "row", E2M1), QuantSpec("qdY_H", "dY", "hadamard", E2M1),
+        ),
+        (
+            GemmSpec("fprop", "qX", "qW", T, 28672, 4096, "bf16"),
+            GemmSpec("dgrad", "qdY", "qW_T", T, 4096, 28672, "bf16"),
+            GemmSpec("wgrad", "qdY_H", "qX_H", 28672, 4096, T, "f32"),
+        ),
+    ),
 )
+
+# the dual-direction quantizations of that layer: (source, row-form operand, transposed-form operand)
+LAYER_DUALS = (("X", "qX", "qX_H"), ("W", "qW", "qW_T"), ("dY", "qdY", "qdY_H"))
 
 
 def config(index_or_name) -> Config:
