@@ -53,6 +53,8 @@ PROFILE_COMMANDS = (
     "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra --iso-reps 5",
     "rocprofv3 --pmc MfmaUtil --output-format csv -d rocprof_out/prof_mfma -o mfma -- "
     "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra --iso-reps 5",
+    "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE --output-format csv -d rocprof_out/prof_lds -o lds -- "
+    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra --iso-reps 5",
 )
 XCDS = 8          # MI355X: GRBM_GUI_ACTIVE sums the busy cycles of the 8 accelerator dies
 PEAK_SCLK_GHZ = 2.4
@@ -467,7 +469,8 @@ def _find(d, suffix):
 
 
 def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir: str, command: str,
-                       out_dir: str = os.path.join(ROOT, "profiles"), mfma_dir: str = None) -> None:
+                       out_dir: str = os.path.join(ROOT, "profiles"), mfma_dir: str = None,
+                       lds_dir: str = None) -> None:
     """Turn rocprofv3 CSV output (kernel trace with stats; FETCH_SIZE and
     WRITE_SIZE counter passes with --calibrate-copy) into the short summaries
     kept under profiles/: per-kernel average durations, and HBM bytes per
@@ -626,10 +629,40 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, clock_dir
             lines.append("| `%s` | %d | %.1f |" % (k, len(timed), util))
         with open(os.path.join(out_dir, "mfma_util_%s.md" % WORKLOAD), "w") as f:
             f.write("\n".join(lines) + "\n")
+    # LDS bank conflicts: cycles the LDS stalled on bank conflicts over the cycles it was busy with
+    # indexed accesses (both summed over the shader engines), over each kernel's timed step launches
+    lds = {}
+    if lds_dir is not None:
+        rows = sorted(_read_csv(_find(lds_dir, "counter_collection.csv")), key=lambda r: int(r["Dispatch_Id"]))
+        first_l = next((int(r["Dispatch_Id"]) for r in rows if "reduce" in r["Kernel_Name"].lower()), None)
+        lsteps = int(re.search(r"--steps (\d+)", command[5]).group(1))
+        perl = {}
+        for r in rows:
+            if "mx::" not in r["Kernel_Name"] or (first_l is not None and int(r["Dispatch_Id"]) >= first_l):
+                continue
+            d = perl.setdefault(r["Kernel_Name"], {}).setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        lines = ["# LDS bank conflicts per kernel (rocprofv3 SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE): %s" % WORKLOAD,
+                 "", "Command (run from the repository root on an MI355X):", "", "    " + command[5], "",
+                 "Both counters are cycles summed over the shader engines. Conflict share = bank-conflict stall "
+                 "cycles / cycles the LDS was busy with indexed accesses, over each kernel's timed step launches "
+                 "(its last %d before the first cache fill). Kernels without LDS traffic are left out." % lsteps, "",
+                 "| kernel | timed launches | LDS busy (Mcycles per launch) | conflict stalls (Mcycles per launch) "
+                 "| conflict share |", "|---|---|---|---|---|"]
+        for k, disp in sorted(perl.items(), key=lambda kv: kv[0]):
+            timed = [disp[i] for i in sorted(disp)][-lsteps:]
+            act = sum(d.get("SQ_LDS_IDX_ACTIVE", 0.0) for d in timed) / len(timed)
+            con = sum(d.get("SQ_LDS_BANK_CONFLICT", 0.0) for d in timed) / len(timed)
+            if act <= 0:
+                continue
+            lds[k] = 100.0 * con / act
+            lines.append("| `%s` | %d | %.2f | %.3f | %.2f%% |" % (k, len(timed), act / 1e6, con / 1e6, lds[k]))
+        with open(os.path.join(out_dir, "lds_bank_conflicts_%s.md" % WORKLOAD), "w") as f:
+            f.write("\n".join(lines) + "\n")
     with open(os.path.join(out_dir, "traffic.json"), "w") as f:
         json.dump({"source_sha": kernel_source_sha(), "workload": WORKLOAD, "fetch_scale": f_scale,
                    "write_scale": w_scale, "kernels": kern, "sclk_ghz": sclk, "mfma_util_pct": mfma,
-                   "commands": command[1:]}, f, indent=1)
+                   "lds_conflict_pct": lds, "commands": command[1:]}, f, indent=1)
 
 
 def ablation(mx, torch, seed: int) -> dict:
@@ -691,6 +724,29 @@ def ablation(mx, torch, seed: int) -> dict:
     return out
 
 
+def write_ablation_summary(abl: dict, path: str, seed: int) -> None:
+    """the ablation's table as markdown, with the command that made it"""
+    lines = ["# Weight-gradient recipe ablation (dW error through the library)", "",
+             "Command (run from the repository root on an MI355X):", "",
+             "    python3 bench.py --ablation --seed %d --ablation-summary %s" % (seed, os.path.relpath(path, ROOT)), "",
+             "%s; metric %s, against the fp64 product of the same bf16 inputs. dY = 1e-3 x Student-t (3 degrees of "
+             "freedom), X ~ N(0, 1), seeded synthetic data (a numerical proxy, not training)." % (
+                 abl["shape"], abl["metric"]), "",
+             "| recipe | relative error, one step | 8 steps: min / max | error of the 8-step average |",
+             "|---|---|---|---|"]
+    for k, v in abl.items():
+        if k in ("shape", "metric"):
+            continue
+        if isinstance(v, dict):
+            avg = next((x for kk, x in v.items() if kk.startswith("error_of")), None)
+            lines.append("| %s | %.4f (mean) | %.4f / %.4f | %s |" % (
+                k.replace("_", " "), v["mean"], v["min"], v["max"], "%.4f" % avg if avg is not None else "-"))
+        else:
+            lines.append("| %s | %.4f | - | (same) |" % (k.replace("_", " "), v))
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def kernel_symbol(name: str) -> str:
     """the kernel symbol a bench launch name runs (GEMMs; other names are returned as they are)"""
     if "mx_gemm" in name:
@@ -717,16 +773,20 @@ def main() -> int:
     ap.add_argument("--ablation", action="store_true",
                     help="only the weight-gradient rotation ablation (dW error of the Wgrad recipes)")
     ap.add_argument("--summarize-profiles", nargs="+", metavar="DIR",
-                    help="write profiles/ summaries from rocprofv3 CSV output (TRACE FETCH WRITE CLOCK [MFMA] "
+                    help="write profiles/ summaries from rocprofv3 CSV output (TRACE FETCH WRITE CLOCK [MFMA [LDS]] "
                          "directories) and exit")
+    ap.add_argument("--ablation-summary", metavar="PATH",
+                    help="with --ablation: also write the table as markdown to PATH")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 256 MiB device copy three times (HBM counter calibration)")
     args = ap.parse_args()
     if args.summarize_profiles:
-        if len(args.summarize_profiles) not in (4, 5):
-            ap.error("--summarize-profiles takes the TRACE, FETCH, WRITE, CLOCK and optionally MFMA directories")
+        if len(args.summarize_profiles) not in (4, 5, 6):
+            ap.error("--summarize-profiles takes the TRACE, FETCH, WRITE, CLOCK and optionally MFMA and LDS "
+                     "directories")
         d = args.summarize_profiles
-        summarize_profiles(*d[:4], command=PROFILE_COMMANDS, mfma_dir=d[4] if len(d) == 5 else None)
+        summarize_profiles(*d[:4], command=PROFILE_COMMANDS, mfma_dir=d[4] if len(d) >= 5 else None,
+                           lds_dir=d[5] if len(d) == 6 else None)
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: the hot path runs on a single MI355X and the library "
@@ -742,7 +802,10 @@ def main() -> int:
     torch.cuda.set_device(0)
 
     if args.ablation:
-        print(json.dumps({"ablation": ablation(mx, torch, args.seed)}), flush=True)
+        abl = ablation(mx, torch, args.seed)
+        print(json.dumps({"ablation": abl}), flush=True)
+        if args.ablation_summary:
+            write_ablation_summary(abl, args.ablation_summary, args.seed)
         return 0
 
     print("bench: building inputs", file=sys.stderr, flush=True)

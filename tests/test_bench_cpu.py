@@ -36,7 +36,7 @@ RUN = [
     (11, CALIB, 131072.0, 262144.0, 60000),
 ]
 CMDS = ("trace --steps 2 --warmup 0", "fetch", "write", "clock --steps 2 --warmup 0",
-        "mfma --steps 2 --warmup 0")
+        "mfma --steps 2 --warmup 0", "lds --steps 2 --warmup 0")
 
 
 def _write(path, header, rows):
@@ -72,6 +72,16 @@ def profile_dirs(tmp_path):
     # MfmaUtil: 40 and 50 % for the step's two GEMM launches, 0 for the quantizer
     mf = [[d, k, "MfmaUtil", (40.0 + 10.0 * (d == 4)) if k == GEMM else 0.0, 0, 1] for d, k, _, _, _ in RUN]
     _write(str(tmp_path / "mfma" / "x_counter_collection.csv"), head, mf)
+    # LDS: the GEMM's two step launches busy 1000 and 3000 cycles with 10 and 50 conflict cycles;
+    # the quantizer uses no LDS
+    lds = []
+    for d, k, _, _, _ in RUN:
+        if k == GEMM:
+            act, con = (1000.0, 10.0) if d == 2 else (3000.0, 50.0)
+        else:
+            act, con = 0.0, 0.0
+        lds += [[d, k, "SQ_LDS_IDX_ACTIVE", act, 0, 1], [d, k, "SQ_LDS_BANK_CONFLICT", con, 0, 1]]
+    _write(str(tmp_path / "lds" / "x_counter_collection.csv"), head, lds)
     return tmp_path
 
 
@@ -126,3 +136,23 @@ def test_mfma_summary(profile_dirs):
     # the mean over the step's two GEMM launches (40 and 50); kernels reading 0 are left out
     assert data["mfma_util_pct"] == {GEMM: pytest.approx(45.0)}
     assert "| 2 | 45.0 |" in open(out / ("mfma_util_%s.md" % bench.WORKLOAD)).read()
+
+
+def test_lds_summary(profile_dirs):
+    out = profile_dirs / "out3"
+    bench.summarize_profiles(*(str(profile_dirs / d) for d in ("trace", "fetch", "write", "clock")),
+                             command=CMDS, out_dir=str(out), mfma_dir=str(profile_dirs / "mfma"),
+                             lds_dir=str(profile_dirs / "lds"))
+    data = json.load(open(out / "traffic.json"))
+    # (10 + 50) / (1000 + 3000) over the step's two GEMM launches; the quantizer (no LDS) is left out
+    assert data["lds_conflict_pct"] == {GEMM: pytest.approx(1.5)}
+    assert "| 2 | 0.00 | 0.000 | 1.50% |" in open(out / ("lds_bank_conflicts_%s.md" % bench.WORKLOAD)).read()
+
+
+def test_ablation_summary(tmp_path):
+    abl = {"shape": "dW[2x2]", "metric": "rel", "plain": 0.25,
+           "random": {"mean": 0.2, "min": 0.1, "max": 0.3, "error_of_the_8_step_average": 0.05}}
+    path = tmp_path / "abl.md"
+    bench.write_ablation_summary(abl, str(path), 0)
+    text = open(path).read()
+    assert "--ablation --seed 0" in text and "| plain | 0.2500 |" in text and "| 0.1000 / 0.3000 | 0.0500 |" in text
