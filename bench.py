@@ -973,7 +973,19 @@ def main() -> int:
     q_x8 = mx.quantize(xg, "e4m3")
     q_w4 = mx.quantize(wg, "e2m1")
     rec("fprop_e4m3_x_e2m1 Y = X W^T", q_x8, "e4m3", q_w4, "e2m1", torch.bfloat16, "bf16")
-    del q_x8
+    # The carrier's exact per-block path: a tile any of whose rows mixes an
+    # all-zero block (scale byte 0) with normal blocks goes to the second
+    # kernel.  The same 8192 x 6144 x 4096 E4M3 GEMM once with the workload's
+    # activations and once with their first 32 columns zeroed, which puts one
+    # all-zero block in every row of X and sends every tile there.
+    q_w8 = mx.quantize(wg[:6144], "e4m3")
+    rec("fprop_e4m3 8192x6144x4096", q_x8, "e4m3", q_w8, "e4m3", torch.bfloat16, "bf16")
+    xz = xg.clone()
+    xz[:, :32] = 0
+    q_xz = mx.quantize(xz, "e4m3")
+    rec("fprop_e4m3 8192x6144x4096, one all-zero block per row of X", q_xz, "e4m3", q_w8, "e4m3",
+        torch.bfloat16, "bf16")
+    del q_x8, q_w8, q_xz, xz
     q_dy5 = mx.quantize(dy, "e5m2")
     q_wt8 = mx.quantize_transpose(wg, "e4m3")
     rec("dgrad_e5m2_x_e4m3 dX = dY W", q_dy5, "e5m2", q_wt8, "e4m3", torch.bfloat16, "bf16")

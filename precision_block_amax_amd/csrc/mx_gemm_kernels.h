@@ -588,27 +588,65 @@ __device__ __forceinline__ void dma16(v4i r, void *lds, int voff, int soff) {
                  : "memory", "m0");
 }
 
-// max and min of a row's E8M0 bytes (uint4 loads when aligned)
-__device__ __forceinline__ void row_scale_range(const uint8_t *p, int n, bool vec, int &mx, int &mn) {
+// Largest of a row's E8M0 bytes, smallest of its nonzero ones (255 if none)
+// and whether any is zero.  With vec (16-byte aligned, n % 16 == 0) the bytes
+// come as uint4 loads, four in flight at a time: the scan runs once per tile
+// and row, before the tile's first stage.
+__device__ __forceinline__ void row_scale_range(const uint8_t *p, int n, bool vec, int &mx, int &mnz, bool &has0) {
     mx = 0;
-    mn = 255;
+    mnz = 255;
+    has0 = false;
+    const auto take = [&](int b) {
+        mx = max(mx, b);
+        if (b) mnz = min(mnz, b);
+        else has0 = true;
+    };
+    const auto take16 = [&](const uint4 &t) {
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int q = 0; q < 16; q++) take((w[q >> 2] >> (8 * (q & 3))) & 0xFF);
+    };
+    if (vec) {
+        int k = 0;
+        for (; k + 64 <= n; k += 64) {
+            uint4 t[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) t[u] = *reinterpret_cast<const uint4 *>(p + k + 16 * u);
+#pragma unroll
+            for (int u = 0; u < 4; u++) take16(t[u]);
+        }
+        for (; k < n; k += 16) take16(*reinterpret_cast<const uint4 *>(p + k));
+    } else {
+        for (int k = 0; k < n; k++) take(p[k]);
+    }
+}
+
+// true if every block of the row whose scale byte is 0 holds only zero codes
+// (either sign: MAG masks the magnitude bits): codes c of the row (16-byte
+// aligned), scales p, n blocks of BB code bytes
+template <int BB, uint32_t MAG>
+__device__ __forceinline__ bool zero_blocks_clear(const uint8_t *c, const uint8_t *p, int n, bool vec) {
+    uint32_t any = 0;
+    const auto check = [&](int k) {
+#pragma unroll
+        for (int q = 0; q < BB; q += 16) {
+            const uint4 t = *reinterpret_cast<const uint4 *>(c + (int64_t)k * BB + q);
+            any |= (t.x | t.y | t.z | t.w) & MAG;
+        }
+    };
     if (vec) {
         for (int k = 0; k < n; k += 16) {
             const uint4 t = *reinterpret_cast<const uint4 *>(p + k);
             const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-            for (int q = 0; q < 16; q++) {
-                const int b = (w[q >> 2] >> (8 * (q & 3))) & 0xFF;
-                mx = max(mx, b);
-                mn = min(mn, b);
-            }
+            for (int q = 0; q < 16; q++)
+                if (((w[q >> 2] >> (8 * (q & 3))) & 0xFF) == 0) check(k + q);
         }
     } else {
-        for (int k = 0; k < n; k++) {
-            mx = max(mx, (int)p[k]);
-            mn = min(mn, (int)p[k]);
-        }
+        for (int k = 0; k < n; k++)
+            if (p[k] == 0) check(k);
     }
+    return any == 0;
 }
 
 // four consecutive columns n .. n+3 of row m
@@ -711,9 +749,22 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
         const bool vec = (kblocks % 16 == 0) && ((((uintptr_t)g.as | (uintptr_t)g.bs) & 15) == 0) &&
                          (((srowA | srowB) & 15) == 0);
         int mx_, mn_;
-        row_scale_range((isA ? g.as : g.bs) + (int64_t)gr * (isA ? srowA : srowB), kblocks, vec, mx_, mn_);
+        bool has0;
+        const uint8_t *ps = (isA ? g.as : g.bs) + (int64_t)gr * (isA ? srowA : srowB);
+        row_scale_range(ps, kblocks, vec, mx_, mn_, has0);
         (isA ? sRa : sRb)[r] = mx_;
-        const bool w = mx_ - mn_ > kSpreadMax || mx_ == 255;
+        bool w = mx_ - mn_ > kSpreadMax || mx_ == 255;
+        if (has0 && mx_ > kSpreadMax && !w) {
+            // A block with scale byte 0 beside blocks more than kSpreadMax binades
+            // above it.  If its codes are all zero it adds exactly 0 under any finite
+            // scale; its rebased byte 127 - R stays in [0, 127] (a finite scale, no
+            // borrow into the neighbouring bytes of the scale word) as long as
+            // R <= 127.  Then the tile keeps the fast path; a block of genuinely tiny
+            // values (nonzero codes under scale byte 0) sends it to the exact kernel.
+            const uint8_t *pc = isA ? g.a + (int64_t)gr * rowA : g.b + (int64_t)gr * rowB;
+            w = mx_ > 127 || !((isA ? A4 : B4) ? zero_blocks_clear<16, 0x77777777u>(pc, ps, kblocks, vec)
+                                                : zero_blocks_clear<32, 0x7F7F7F7Fu>(pc, ps, kblocks, vec));
+        }
         if (__syncthreads_or(w) != 0) {  // uniform across the workgroup
             if (tid == 0) mark_tile<BF16OUT>(g, m0, n0);
             return;

@@ -306,3 +306,45 @@ def test_scale_spreads(mx, fa, fb, spread):
         c = _host_c(_run(mx, (ca, sa), fa, (cb, sb), fb, bf16), bf16)
         r = check_gemm(c, C, S, bf16)
         print(spread, fa, fb, "bf16" if bf16 else "f32", "max |err|/S", r)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e2m1")])
+@pytest.mark.parametrize("case", ["zero_blocks", "zero_blocks_high_R", "tiny_blocks"])
+def test_carrier_blocks_under_scale_zero(mx, fa, fb, case):
+    """blocks whose E8M0 byte is 0 in rows whose other blocks lie 100+ binades
+    higher (pipelined carrier, K = 1024).  All-zero blocks (codes of either
+    sign) add exactly 0 and leave their tile on the fast path while the row's
+    largest byte R <= 127; with R up to 135 the tile must take the exact
+    per-block kernel (a rebased zero byte would borrow from its neighbours);
+    a block of tiny nonzero values under byte 0 must take it too."""
+    rng = np.random.default_rng(["zero_blocks", "zero_blocks_high_R", "tiny_blocks"].index(case) * 10
+                                + FMTS.index(fa) + 3 * FMTS.index(fb))
+    M, N, K = 300, 272, 1024
+    kb = K // 32
+    ca, cb = _random_codes(rng, M, K, fa), _random_codes(rng, N, K, fb)
+    hi = 136 if case == "zero_blocks_high_R" else 128
+    sa = rng.integers(hi - 30, hi, (M, kb)).astype(np.uint8)
+    sb = rng.integers(hi - 30, hi, (N, kb)).astype(np.uint8)
+
+    def clear(c, s, rows, blocks, fmt):
+        nb = 16 if fmt == "e2m1" else 32
+        neg = 0x88 if fmt == "e2m1" else 0x80
+        for r, b in zip(rows, blocks):
+            s[r, b] = 0
+            c[r, b * nb:(b + 1) * nb] = neg if r % 3 == 0 else 0  # negative zeros in some rows
+
+    rows_a = np.arange(0, M, 2)                      # every other row of A: one zero block
+    clear(ca, sa, rows_a, rng.integers(0, kb, rows_a.size), fa)
+    rows_b = np.arange(1, N, 5)
+    clear(cb, sb, rows_b, rng.integers(0, kb, rows_b.size), fb)
+    if case == "tiny_blocks":                        # a few byte-0 blocks keep nonzero codes
+        for r in (4, 130, 262):
+            b = int(rng.integers(0, kb))
+            sa[r, b] = 0
+    C, S = oracle.gemm(ca, sa, fa, cb, sb, fb)
+    print("case", case, fa, fb, flush=True)
+    for bf16 in (False, True):
+        c = _host_c(_run(mx, (ca, sa), fa, (cb, sb), fb, bf16), bf16)
+        assert not np.isnan(c).any(), "NaN in C"
+        r = check_gemm(c, C, S, bf16)
+        print(case, fa, fb, "bf16" if bf16 else "f32", "max |err|/S", r, flush=True)
