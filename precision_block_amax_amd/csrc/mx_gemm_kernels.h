@@ -333,18 +333,35 @@ __device__ __forceinline__ v8bf to_bf16x8(uint32_t lo, uint32_t hi, float scale)
     return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// the 8 codes of row `row`, elements [16s + 8h, 16s + 8h + 8) of the K tile
+// The codes a lane multiplies at step s (16 K per bf16 instruction): lane
+// group h takes 16 consecutive codes of the step pair's 32-element block,
+// the first 8 at the even step and the last 8 at the odd one.  A and B use
+// the same order, so each instruction still pairs equal K, and both steps
+// stay inside one block.  read_codes2 fetches both steps' codes at once: one
+// 16-byte LDS read per lane (8 bytes for E2M1), whose 16-lane passes hit
+// 16 different bank groups under the tile's swizzle.
 template <int F, int RB>
 __device__ __forceinline__ void read_codes(const uint8_t *tile, int row, int s, int h, uint32_t &lo, uint32_t &hi) {
     if constexpr (F == E2M1) {
-        const int byte = 8 * s + 4 * h;  // 4 bytes
+        const int byte = 16 * (s >> 1) + 8 * h + 4 * (s & 1);  // 4 bytes
         lo = *reinterpret_cast<const uint32_t *>(&tile[swz<RB>(row, byte >> 4) + (byte & 15)]);
         hi = 0;
     } else {
-        const int byte = 16 * s + 8 * h;  // 8 bytes
+        const int byte = 32 * (s >> 1) + 16 * h + 8 * (s & 1);  // 8 bytes
         const uint2 t = *reinterpret_cast<const uint2 *>(&tile[swz<RB>(row, byte >> 4) + (byte & 15)]);
         lo = t.x;
         hi = t.y;
+    }
+}
+template <int F, int RB>
+__device__ __forceinline__ uint4 read_codes2(const uint8_t *tile, int row, int j, int h) {
+    if constexpr (F == E2M1) {
+        const int byte = 16 * j + 8 * h;  // 8 bytes: steps 2j (x) and 2j + 1 (y)
+        const uint2 t = *reinterpret_cast<const uint2 *>(&tile[swz<RB>(row, byte >> 4) + (byte & 15)]);
+        return make_uint4(t.x, 0u, t.y, 0u);
+    } else {
+        const int byte = 32 * j + 16 * h;  // 16 bytes: steps 2j (x, y) and 2j + 1 (z, w)
+        return *reinterpret_cast<const uint4 *>(&tile[swz<RB>(row, byte >> 4)]);
     }
 }
 
@@ -913,8 +930,9 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
                 const int rb_ = wn * 64 + j * 32 + l32;
                 db[j] = rebase(*reinterpret_cast<const uint32_t *>(&tSB[rb_ * 16]), sRb[rb_]);
             }
-            // Software-pipelined: step t + 1's codes are read from LDS at the top of step t
-            // and converted in the shadow of step t's MFMAs.  The MFMAs go column by
+            // Software-pipelined: the codes of a step pair are read from LDS (one 16-byte
+            // read per fragment) at the top of the step before the pair, and step t + 1's
+            // fragments are converted in the shadow of step t's MFMAs.  The MFMAs go column by
             // column: the four on B fragment 0 first (they cover the LDS latency), then B
             // fragment 0 of step t + 1 is converted into the registers they released, and
             // each A fragment of step t + 1 right after the last MFMA that reads its
@@ -922,41 +940,39 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
             // just before their own MFMAs, with both waves of a SIMD released by the same
             // barrier, the conversions and the matrix work had run one after the other.)
             v8bf fa[4], fb[2];
-            {
-                uint32_t alo[4], ahi[4], blo[2], bhi[2];
+            uint4 ca[4], cb[2];  // codes of the current step pair
+            const auto rd = [&](int j) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, 0, h, alo[i], ahi[i]);
+                for (int jj = 0; jj < 2; jj++) cb[jj] = read_codes2<FB, RBB>(tB, wn * 64 + jj * 32 + l32, j, h);
 #pragma unroll
-                for (int j = 0; j < 2; j++) read_codes<FB, RBB>(tB, wn * 64 + j * 32 + l32, 0, h, blo[j], bhi[j]);
-                issue_next();
+                for (int i = 0; i < 4; i++) ca[i] = read_codes2<FA, RBA>(tA, wm * 128 + i * 32 + l32, j, h);
+            };
+            const auto lo_of = [](const uint4 &c, int odd) { return odd ? c.z : c.x; };
+            const auto hi_of = [](const uint4 &c, int odd) { return odd ? c.w : c.y; };
+            rd(0);
+            issue_next();
 #pragma unroll
-                for (int i = 0; i < 4; i++) fa[i] = to_bf16x8<FA>(alo[i], ahi[i], block_scale(da[i], 0));
+            for (int i = 0; i < 4; i++) fa[i] = to_bf16x8<FA>(ca[i].x, ca[i].y, block_scale(da[i], 0));
 #pragma unroll
-                for (int j = 0; j < 2; j++) fb[j] = to_bf16x8<FB>(blo[j], bhi[j], block_scale(db[j], 0));
-            }
+            for (int j = 0; j < 2; j++) fb[j] = to_bf16x8<FB>(cb[j].x, cb[j].y, block_scale(db[j], 0));
             __builtin_amdgcn_sched_barrier(0);
             static_for<0, KE / 16>([&](auto step) {
                 constexpr int t = decltype(step)::value;
                 constexpr bool more = t + 1 < KE / 16;
-                uint32_t alo[4], ahi[4], blo[2], bhi[2];
-                if constexpr (more) {
-#pragma unroll
-                    for (int j = 0; j < 2; j++) read_codes<FB, RBB>(tB, wn * 64 + j * 32 + l32, t + 1, h, blo[j], bhi[j]);
-#pragma unroll
-                    for (int i = 0; i < 4; i++) read_codes<FA, RBA>(tA, wm * 128 + i * 32 + l32, t + 1, h, alo[i], ahi[i]);
-                }
+                constexpr int odd = (t + 1) & 1;  // step t + 1 takes the second half of its pair
+                if constexpr (more && odd == 0) rd((t + 1) >> 1);
 #pragma unroll
                 for (int i = 0; i < 4; i++)
                     acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0], fa[i], acc[i][0], 0, 0, 0);
-                if constexpr (more) fb[0] = to_bf16x8<FB>(blo[0], bhi[0], block_scale(db[0], (t + 1) >> 1));
+                if constexpr (more) fb[0] = to_bf16x8<FB>(lo_of(cb[0], odd), hi_of(cb[0], odd), block_scale(db[0], (t + 1) >> 1));
                 __builtin_amdgcn_sched_barrier(0);
                 static_for<0, 4>([&](auto ii) {
                     constexpr int i = decltype(ii)::value;
                     acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1], fa[i], acc[i][1], 0, 0, 0);
-                    if constexpr (more) fa[i] = to_bf16x8<FA>(alo[i], ahi[i], block_scale(da[i], (t + 1) >> 1));
+                    if constexpr (more) fa[i] = to_bf16x8<FA>(lo_of(ca[i], odd), hi_of(ca[i], odd), block_scale(da[i], (t + 1) >> 1));
                     __builtin_amdgcn_sched_barrier(0);
                 });
-                if constexpr (more) fb[1] = to_bf16x8<FB>(blo[1], bhi[1], block_scale(db[1], (t + 1) >> 1));
+                if constexpr (more) fb[1] = to_bf16x8<FB>(lo_of(cb[1], odd), hi_of(cb[1], odd), block_scale(db[1], (t + 1) >> 1));
                 __builtin_amdgcn_sched_barrier(0);
             });
         } else {
