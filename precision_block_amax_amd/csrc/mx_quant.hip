@@ -78,13 +78,16 @@ template <int F, bool ROTATE>
 hipError_t launch_tr_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint32_t mask,
                          uint8_t *codes, uint8_t *scales, hipStream_t stream) {
     const bool vec = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0) && ((uintptr_t)codes % 16 == 0);
-    const dim3 grid((unsigned)((cols + kTrCols - 1) / kTrCols), (unsigned)((rows / 32 + kTrBlocks - 1) / kTrBlocks));
-    if (vec)
-        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true>), grid, dim3(64 * kTrWaves), 0, stream, x, ldx,
-                           rows, cols, mask, codes, scales);
-    else
-        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, false>), grid, dim3(64 * kTrWaves), 0, stream, x,
-                           ldx, rows, cols, mask, codes, scales);
+    const unsigned tx = (unsigned)((cols + kTrCols - 1) / kTrCols);
+    if (vec) {
+        constexpr int W = tr_waves<F, true, -1, false>();
+        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true>), dim3(tx, (unsigned)((rows / 32 + W - 1) / W)),
+                           dim3(64 * W), 0, stream, x, ldx, rows, cols, mask, codes, scales);
+    } else {
+        constexpr int W = tr_waves<F, false, -1, false>();
+        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, false>), dim3(tx, (unsigned)((rows / 32 + W - 1) / W)),
+                           dim3(64 * W), 0, stream, x, ldx, rows, cols, mask, codes, scales);
+    }
     return hipGetLastError();
 }
 
@@ -92,12 +95,14 @@ template <int F, bool ROTATE>
 hipError_t launch_tr_sr_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint32_t mask, uint64_t seed,
                             uint8_t *codes, uint8_t *scales, hipStream_t stream) {
     const bool vec = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0) && ((uintptr_t)codes % 16 == 0);
-    const dim3 grid((unsigned)((cols + kTrCols - 1) / kTrCols), (unsigned)((rows / 32 + kTrBlocks - 1) / kTrBlocks));
+    constexpr int W = tr_waves<F, true, -1, true>();
+    static_assert(W == tr_waves<F, false, -1, true>(), "one grid for both variants");
+    const dim3 grid((unsigned)((cols + kTrCols - 1) / kTrCols), (unsigned)((rows / 32 + W - 1) / W));
     if (vec)
-        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true, -1, true>), grid, dim3(64 * kTrWaves), 0, stream,
+        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true, -1, true>), grid, dim3(64 * W), 0, stream,
                            x, ldx, rows, cols, mask, codes, scales, nullptr, nullptr, seed);
     else
-        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, false, -1, true>), grid, dim3(64 * kTrWaves), 0, stream,
+        hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, false, -1, true>), grid, dim3(64 * W), 0, stream,
                            x, ldx, rows, cols, mask, codes, scales, nullptr, nullptr, seed);
     return hipGetLastError();
 }
@@ -138,9 +143,10 @@ hipError_t launch_tr_pair_fmt(const QuantJob &a, const QuantJob &b, uint32_t mas
         return e != hipSuccess ? e : launch_tr_fmt<F, ROTATE>(b.x, b.rows, b.cols, b.ldx, mask, b.codes, b.scales, stream);
     }
     const uint32_t tx = (uint32_t)((a.cols + kTrCols - 1) / kTrCols), ux = (uint32_t)((b.cols + kTrCols - 1) / kTrCols);
-    const int64_t ra = (a.rows / 32 + kTrBlocks - 1) / kTrBlocks, rb = (b.rows / 32 + kTrBlocks - 1) / kTrBlocks;
+    constexpr int W = tr_waves<F, true, -1, false>();
+    const int64_t ra = (a.rows / 32 + W - 1) / W, rb = (b.rows / 32 + W - 1) / W;
     const dim3 grid(tx + ux, (unsigned)(ra > rb ? ra : rb));
-    hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true, -1, false, true>), grid, dim3(64 * kTrWaves), 0, stream,
+    hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true, -1, false, true>), grid, dim3(64 * W), 0, stream,
                        a.x, a.ldx, a.rows, a.cols, mask, a.codes, a.scales, nullptr, nullptr, (uint64_t)0,
                        b.x, b.ldx, b.rows, b.cols, b.codes, b.scales, tx);
     return hipGetLastError();

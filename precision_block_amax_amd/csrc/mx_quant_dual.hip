@@ -16,12 +16,14 @@ hipError_t launch_dual_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_
                            hipStream_t stream) {
     const bool vec = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0) && ((uintptr_t)codes_t % 16 == 0) &&
                      ((uintptr_t)codes_r % 16 == 0);
-    const dim3 grid((unsigned)((cols + kTrCols - 1) / kTrCols), (unsigned)((rows / 32 + kTrBlocks - 1) / kTrBlocks));
+    constexpr int W = tr_waves<FT, true, FR, false>();
+    static_assert(W == tr_waves<FT, false, FR, false>(), "one grid for both variants");
+    const dim3 grid((unsigned)((cols + kTrCols - 1) / kTrCols), (unsigned)((rows / 32 + W - 1) / W));
     if (vec)
-        hipLaunchKernelGGL((k_quantize_transpose<FT, ROTATE, true, FR>), grid, dim3(64 * kTrWaves), 0, stream, x,
+        hipLaunchKernelGGL((k_quantize_transpose<FT, ROTATE, true, FR>), grid, dim3(64 * W), 0, stream, x,
                            ldx, rows, cols, mask, codes_t, scales_t, codes_r, scales_r);
     else
-        hipLaunchKernelGGL((k_quantize_transpose<FT, ROTATE, false, FR>), grid, dim3(64 * kTrWaves), 0, stream, x,
+        hipLaunchKernelGGL((k_quantize_transpose<FT, ROTATE, false, FR>), grid, dim3(64 * W), 0, stream, x,
                            ldx, rows, cols, mask, codes_t, scales_t, codes_r, scales_r);
     return hipGetLastError();
 }

@@ -194,14 +194,19 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
 // c0 .. c0+3 of one 32-row block at a time (one 8-byte load per row, each
 // wave instruction reading 512 contiguous bytes of a row), so the block's
 // amax and the rotation's butterflies stay in the lane's registers.  A
-// workgroup covers 256 columns x 8 row blocks, one block per wave.  The codes
-// are staged in LDS and written out afterwards as whole
-// 128-byte (E2M1) or 256-byte (FP8) runs of each output row, and the 8 scale
-// bytes of each output row as one 8-byte store.
+// workgroup covers 256 columns x W row blocks, one block per wave (W below).
+// The codes are staged in LDS and written out afterwards as whole runs of W
+// blocks of each output row (128 bytes for E2M1, 512 for FP8 with W = 16),
+// and the W scale bytes of each output row as one store.
 constexpr int kTrColsPerLane = 4;
-constexpr int kTrWaves = 8;
-constexpr int kTrBlocks = 8;   // row blocks per workgroup
 constexpr int kTrCols = 256;   // columns per workgroup
+// Waves per workgroup, one row block each.  FP8 codes alone: 16, so each
+// output row leaves as a 512-byte run (measured 8% faster than 8 waves with
+// 256-byte runs on the 8192 x 8192 weight).  E2M1 (128-byte runs), the fused
+// row form, stochastic rounding and unaligned inputs: 8 (16 waves measured
+// 10-15% slower for E2M1; the others do not fit 16 waves' registers or LDS).
+template <int F, bool VEC, int FR, bool SR>
+constexpr int tr_waves() { return (F != E2M1 && VEC && FR < 0 && !SR) ? 16 : 8; }
 
 // y = c * H32 * diag(s) * x, stages h = 1, 2, 4, 8, 16, one fp32 rounding per op
 __device__ __forceinline__ void hadamard32(float (&y)[32], uint32_t sign_mask) {
@@ -303,7 +308,7 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 // taller of the two, and a workgroup past its tensor's last row block writes
 // nothing.
 template <int F, bool ROTATE, bool VEC, int FR = -1, bool SR = false, bool PAIR = false>
-__global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
+__global__ __launch_bounds__((64 * tr_waves<F, VEC, FR, SR>())) void k_quantize_transpose(
     const uint16_t *__restrict__ x, int64_t ldx, int64_t rows, int64_t cols, uint32_t sign_mask,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_r = nullptr,
     uint8_t *__restrict__ scales_r = nullptr, uint64_t seed = 0, const uint16_t *__restrict__ x1 = nullptr,
@@ -311,6 +316,7 @@ __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
     uint8_t *__restrict__ scales1 = nullptr, uint32_t split = 0) {
     static_assert(!(SR && FR >= 0), "stochastic rounding is a transposed-form variant");
     static_assert(!(PAIR && (SR || FR >= 0)), "pairs of the plain and rotated transposed forms only");
+    constexpr int kTrWaves = tr_waves<F, VEC, FR, SR>(), kTrBlocks = kTrWaves;
     uint32_t bx = blockIdx.x;
     if (PAIR && bx >= split) {  // uniform across the workgroup
         bx -= split;
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
     constexpr int CB = kTrBlocks * BB;                  // staged bytes per output row: 128 or 256
     constexpr int NCH = CB / 16;                        // 16-byte chunks per output row
     __shared__ __attribute__((aligned(16))) uint8_t sC[kTrCols * CB];
-    __shared__ __attribute__((aligned(8))) uint8_t sS[kTrCols * kTrBlocks];
+    __shared__ __attribute__((aligned(16))) uint8_t sS[kTrCols * kTrBlocks];
     // row form: per wave 32 rows x RB code bytes, then 32 rows x 8 scale bytes
     constexpr int RB = FR == E2M1 ? 128 : 256;
     constexpr int RSTAGE = FR >= 0 ? kTrWaves * 32 * (RB + 8) : 16;
@@ -514,7 +520,9 @@ __global__ __launch_bounds__(64 * kTrWaves) void k_quantize_transpose(
         const int c = threadIdx.x;  // one output row's 8 scale bytes per thread
         if (c < nc) {
             uint8_t *dst = scales + (ctile + c) * nrb + rb0;
-            if (nb == kTrBlocks && (((uintptr_t)dst & 7) == 0)) {
+            if (kTrBlocks == 16 && nb == kTrBlocks && (((uintptr_t)dst & 15) == 0)) {
+                *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&sS[c * kTrBlocks]);
+            } else if (kTrBlocks == 8 && nb == kTrBlocks && (((uintptr_t)dst & 7) == 0)) {
                 *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(&sS[c * kTrBlocks]);
             } else {
                 for (int i = 0; i < nb; i++) dst[i] = sS[c * kTrBlocks + i];
