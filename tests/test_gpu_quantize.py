@@ -150,8 +150,11 @@ def test_row_ragged_strided(mx, fmt, rows, cols, extra):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rotate", [False, True])
 @pytest.mark.parametrize("rows,cols,extra", [(32, 1, 0), (64, 37, 0), (96, 255, 0), (160, 258, 0),
-                                             (32, 1030, 0), (64, 16, 5), (224, 300, 2)])
+                                             (32, 1030, 0), (64, 16, 5), (224, 300, 2),
+                                             (544, 300, 0), (800, 1030, 2), (1056, 260, 4)])
 def test_transposed_ragged_strided(mx, fmt, rotate, rows, cols, extra):
+    """ragged and strided shapes; the last three span several workgroup row groups
+    (8 or 16 row blocks each) with a partial last group"""
     full = _rand_bits(rows, cols + extra, rows * 7 + cols)
     xd = to_dev_bf16(full)[:, :cols]
     x = np.ascontiguousarray(full[:, :cols])
