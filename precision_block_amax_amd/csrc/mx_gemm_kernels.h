@@ -42,8 +42,9 @@
 // (V_CVT_SCALEF32_PK_BF16_{FP8,BF8,FP4}: two codes per instruction, exact for
 // normal power-of-two scales), same for B, and C = 2^(R_a + R_b - 254) *
 // sum a' b'.  A tile in which some row's scales spread over more than 40
-// binades, or which holds an E8M0 NaN (0xFF), is left to a second kernel with
-// an exact per-block path: each 32-element block's partial sum of unscaled
+// binades (the pipelined kernel leaves all-zero blocks out of the spread), or
+// which holds an E8M0 NaN (0xFF), is left to a second kernel with an exact
+// per-block path: each 32-element block's partial sum of unscaled
 // codes is scaled with ldexp and added in fp32 (separate kernels keep the
 // VALU-side accumulation out of the fast kernel's register budget).
 #pragma once
