@@ -16,6 +16,19 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
+// An enum parameter's value as the caller passed it.  A C caller may pass any
+// int through an enum type, but in C++ a load of an enum object whose value
+// lies outside its enumerators' range has no defined meaning; the entry
+// points therefore read their enum parameters' bytes as an int and validate
+// that.
+template <class E>
+int raw(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "the ABI's enums are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 bool fmt_ok(int f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; }
 
 int64_t code_bytes(int64_t n, int fmt) { return fmt == MX_E2M1 ? n / 2 : n; }
@@ -112,12 +125,25 @@ mx_status_t check_gemm(const void *a_codes, int64_t lda, const void *a_scales, i
     return MX_OK;
 }
 
+// mx_gemm_strided with its enum arguments already read as ints
+mx_status_t gemm_strided(const void *a_codes, int64_t lda, const void *a_scales, int64_t ldsa, int fa,
+                         const void *b_codes, int64_t ldb, const void *b_scales, int64_t ldsb, int fb, int64_t M,
+                         int64_t N, int64_t K, void *c, int out, int64_t ldc, void *stream) {
+    mx_status_t st = check_gemm(a_codes, lda, a_scales, ldsa, fa, b_codes, ldb, b_scales, ldsb, fb, M, N, K, c, out,
+                                ldc);
+    if (st != MX_OK || M == 0 || N == 0) return st;
+    if ((st = check_device()) != MX_OK) return st;
+    return launched(mx::launch_gemm((const uint8_t *)a_codes, lda, (const uint8_t *)a_scales, ldsa, fa,
+                                    (const uint8_t *)b_codes, ldb, (const uint8_t *)b_scales, ldsb, fb, M, N, K, c,
+                                    out == MX_OUT_BF16, ldc, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
 
 const char *mx_status_string(mx_status_t s) {
-    switch (s) {
+    switch (raw(s)) {
     case MX_OK: return "MX_OK";
     case MX_ERR_INVALID_ARG: return "MX_ERR_INVALID_ARG";
     case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
@@ -130,29 +156,32 @@ int mx_version(void) { return 100; }
 
 mx_status_t mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt,
                         void *codes, void *scales, void *stream) {
-    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt, codes, scales, false);
+    const int f = raw(fmt);
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, f, codes, scales, false);
     if (st != MX_OK || rows == 0 || cols == 0) return st;
     if ((st = check_device()) != MX_OK) return st;
-    return launched(mx::launch_quantize_rows((const uint16_t *)x_bf16, rows, cols, ldx, fmt, (uint8_t *)codes,
+    return launched(mx::launch_quantize_rows((const uint16_t *)x_bf16, rows, cols, ldx, f, (uint8_t *)codes,
                                              (uint8_t *)scales, (hipStream_t)stream));
 }
 
 mx_status_t mx_quantize_transpose(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
                                   mx_format_t fmt, void *codes, void *scales, void *stream) {
-    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt, codes, scales, true);
+    const int f = raw(fmt);
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, f, codes, scales, true);
     if (st != MX_OK || rows == 0 || cols == 0) return st;
     if ((st = check_device()) != MX_OK) return st;
-    return launched(mx::launch_quantize_transpose((const uint16_t *)x_bf16, rows, cols, ldx, fmt, false, 0,
+    return launched(mx::launch_quantize_transpose((const uint16_t *)x_bf16, rows, cols, ldx, f, false, 0,
                                                   (uint8_t *)codes, (uint8_t *)scales, (hipStream_t)stream));
 }
 
 mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
                                    uint32_t sign_mask, mx_format_t fmt, void *codes, void *scales,
                                    void *stream) {
-    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt, codes, scales, true);
+    const int f = raw(fmt);
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, f, codes, scales, true);
     if (st != MX_OK || rows == 0 || cols == 0) return st;
     if ((st = check_device()) != MX_OK) return st;
-    return launched(mx::launch_quantize_transpose((const uint16_t *)x_bf16, rows, cols, ldx, fmt, true,
+    return launched(mx::launch_quantize_transpose((const uint16_t *)x_bf16, rows, cols, ldx, f, true,
                                                   sign_mask, (uint8_t *)codes, (uint8_t *)scales,
                                                   (hipStream_t)stream));
 }
@@ -160,11 +189,12 @@ mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t col
 mx_status_t mx_quantize_transpose_sr(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, int rotate,
                                      uint32_t sign_mask, uint64_t seed, mx_format_t fmt, void *codes, void *scales,
                                      void *stream) {
+    const int f = raw(fmt);
     if (rotate != 0 && rotate != 1) return MX_ERR_INVALID_ARG;
-    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt, codes, scales, true);
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, f, codes, scales, true);
     if (st != MX_OK || rows == 0 || cols == 0) return st;
     if ((st = check_device()) != MX_OK) return st;
-    return launched(mx::launch_quantize_transpose_sr((const uint16_t *)x_bf16, rows, cols, ldx, fmt, rotate != 0,
+    return launched(mx::launch_quantize_transpose_sr((const uint16_t *)x_bf16, rows, cols, ldx, f, rotate != 0,
                                                      sign_mask, seed, (uint8_t *)codes, (uint8_t *)scales,
                                                      (hipStream_t)stream));
 }
@@ -172,37 +202,41 @@ mx_status_t mx_quantize_transpose_sr(const void *x_bf16, int64_t rows, int64_t c
 mx_status_t mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt_row,
                              void *codes_row, void *scales_row, mx_format_t fmt_t, int rotate, uint32_t sign_mask,
                              void *codes_t, void *scales_t, void *stream) {
+    const int fr = raw(fmt_row);
+    const int ft = raw(fmt_t);
     if (rotate != 0 && rotate != 1) return MX_ERR_INVALID_ARG;
-    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fmt_row, codes_row, scales_row, false);
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fr, codes_row, scales_row, false);
     if (st != MX_OK) return st;
-    if ((st = check_quant(x_bf16, rows, cols, ldx, fmt_t, codes_t, scales_t, true)) != MX_OK) return st;
+    if ((st = check_quant(x_bf16, rows, cols, ldx, ft, codes_t, scales_t, true)) != MX_OK) return st;
     if (rows == 0 || cols == 0) return MX_OK;
     const int64_t n = rows * cols;
-    const int64_t crb = code_bytes(n, fmt_row), ctb = code_bytes(n, fmt_t), sb = n / 32;
+    const int64_t crb = code_bytes(n, fr), ctb = code_bytes(n, ft), sb = n / 32;
     if (overlap(codes_row, crb, codes_t, ctb) || overlap(codes_row, crb, scales_t, sb) ||
         overlap(scales_row, sb, codes_t, ctb) || overlap(scales_row, sb, scales_t, sb))
         return MX_ERR_INVALID_ARG;
     if ((st = check_device()) != MX_OK) return st;
-    return launched(mx::launch_quantize_dual((const uint16_t *)x_bf16, rows, cols, ldx, fmt_row, (uint8_t *)codes_row,
-                                             (uint8_t *)scales_row, fmt_t, rotate != 0, sign_mask, (uint8_t *)codes_t,
+    return launched(mx::launch_quantize_dual((const uint16_t *)x_bf16, rows, cols, ldx, fr, (uint8_t *)codes_row,
+                                             (uint8_t *)scales_row, ft, rotate != 0, sign_mask, (uint8_t *)codes_t,
                                              (uint8_t *)scales_t, (hipStream_t)stream));
 }
 
 mx_status_t mx_quantize_pair(mx_pair_mode_t mode, mx_format_t fmt, uint32_t sign_mask, const void *x0,
                              int64_t rows0, int64_t cols0, int64_t ldx0, void *codes0, void *scales0, const void *x1,
                              int64_t rows1, int64_t cols1, int64_t ldx1, void *codes1, void *scales1, void *stream) {
-    if (mode != MX_PAIR_ROW && mode != MX_PAIR_TRANSPOSE && mode != MX_PAIR_HADAMARD) return MX_ERR_INVALID_ARG;
-    const bool tr = mode != MX_PAIR_ROW;
-    mx_status_t st = check_quant(x0, rows0, cols0, ldx0, fmt, codes0, scales0, tr);
+    const int m = raw(mode);
+    const int f = raw(fmt);
+    if (m != MX_PAIR_ROW && m != MX_PAIR_TRANSPOSE && m != MX_PAIR_HADAMARD) return MX_ERR_INVALID_ARG;
+    const bool tr = m != MX_PAIR_ROW;
+    mx_status_t st = check_quant(x0, rows0, cols0, ldx0, f, codes0, scales0, tr);
     if (st != MX_OK) return st;
-    if ((st = check_quant(x1, rows1, cols1, ldx1, fmt, codes1, scales1, tr)) != MX_OK) return st;
+    if ((st = check_quant(x1, rows1, cols1, ldx1, f, codes1, scales1, tr)) != MX_OK) return st;
     const bool e0 = rows0 == 0 || cols0 == 0, e1 = rows1 == 0 || cols1 == 0;
     if (e0 && e1) return MX_OK;
     if (!e0 && !e1) {
         // no output of one tensor may overlap the other tensor's input or outputs
         const int64_t n0 = rows0 * cols0, n1 = rows1 * cols1;
         const int64_t xb0 = ((rows0 - 1) * ldx0 + cols0) * 2, xb1 = ((rows1 - 1) * ldx1 + cols1) * 2;
-        const int64_t cb0 = code_bytes(n0, fmt), cb1 = code_bytes(n1, fmt), sb0 = n0 / 32, sb1 = n1 / 32;
+        const int64_t cb0 = code_bytes(n0, f), cb1 = code_bytes(n1, f), sb0 = n0 / 32, sb1 = n1 / 32;
         if (overlap(codes0, cb0, x1, xb1) || overlap(codes0, cb0, codes1, cb1) || overlap(codes0, cb0, scales1, sb1) ||
             overlap(scales0, sb0, x1, xb1) || overlap(scales0, sb0, codes1, cb1) || overlap(scales0, sb0, scales1, sb1) ||
             overlap(codes1, cb1, x0, xb0) || overlap(scales1, sb1, x0, xb0))
@@ -214,37 +248,34 @@ mx_status_t mx_quantize_pair(mx_pair_mode_t mode, mx_format_t fmt, uint32_t sign
     const mx::QuantJob j1{(const uint16_t *)x1, rows1, cols1, ldx1, (uint8_t *)codes1, (uint8_t *)scales1};
     if (e0 || e1) {  // one tensor: the single call
         const mx::QuantJob &j = e0 ? j1 : j0;
-        if (!tr) return launched(mx::launch_quantize_rows(j.x, j.rows, j.cols, j.ldx, fmt, j.codes, j.scales, s));
-        return launched(mx::launch_quantize_transpose(j.x, j.rows, j.cols, j.ldx, fmt, mode == MX_PAIR_HADAMARD,
+        if (!tr) return launched(mx::launch_quantize_rows(j.x, j.rows, j.cols, j.ldx, f, j.codes, j.scales, s));
+        return launched(mx::launch_quantize_transpose(j.x, j.rows, j.cols, j.ldx, f, m == MX_PAIR_HADAMARD,
                                                       sign_mask, j.codes, j.scales, s));
     }
-    return launched(mx::launch_quantize_pair((int)mode, fmt, mode == MX_PAIR_HADAMARD ? sign_mask : 0u, j0, j1, s));
+    return launched(mx::launch_quantize_pair((int)m, f, m == MX_PAIR_HADAMARD ? sign_mask : 0u, j0, j1, s));
 }
 
 mx_status_t mx_gemm(const void *a_codes, const void *a_scales, mx_format_t fa, const void *b_codes,
                     const void *b_scales, mx_format_t fb, int64_t M, int64_t N, int64_t K, void *c,
                     mx_out_t out, int64_t ldc, void *stream) {
-    if (!fmt_ok(fa) || !fmt_ok(fb) || K < 0) return MX_ERR_INVALID_ARG;
-    return mx_gemm_strided(a_codes, code_bytes(K, fa), a_scales, K / 32, fa, b_codes, code_bytes(K, fb), b_scales,
-                           K / 32, fb, M, N, K, c, out, ldc, stream);
+    const int a = raw(fa), b = raw(fb);
+    if (!fmt_ok(a) || !fmt_ok(b) || K < 0) return MX_ERR_INVALID_ARG;
+    return gemm_strided(a_codes, code_bytes(K, a), a_scales, K / 32, a, b_codes, code_bytes(K, b), b_scales, K / 32,
+                        b, M, N, K, c, raw(out), ldc, stream);
 }
 
 mx_status_t mx_gemm_strided(const void *a_codes, int64_t lda, const void *a_scales, int64_t ldsa, mx_format_t fa,
                             const void *b_codes, int64_t ldb, const void *b_scales, int64_t ldsb, mx_format_t fb,
                             int64_t M, int64_t N, int64_t K, void *c, mx_out_t out, int64_t ldc, void *stream) {
-    mx_status_t st = check_gemm(a_codes, lda, a_scales, ldsa, fa, b_codes, ldb, b_scales, ldsb, fb, M, N, K, c, out,
-                                ldc);
-    if (st != MX_OK || M == 0 || N == 0) return st;
-    if ((st = check_device()) != MX_OK) return st;
-    return launched(mx::launch_gemm((const uint8_t *)a_codes, lda, (const uint8_t *)a_scales, ldsa, fa,
-                                    (const uint8_t *)b_codes, ldb, (const uint8_t *)b_scales, ldsb, fb, M, N, K, c,
-                                    out == MX_OUT_BF16, ldc, (hipStream_t)stream));
+    return gemm_strided(a_codes, lda, a_scales, ldsa, raw(fa), b_codes, ldb, b_scales, ldsb, raw(fb), M, N, K, c,
+                        raw(out), ldc, stream);
 }
 
 mx_status_t mx_quantize_strided(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt,
                                 void *codes, int64_t ld_codes, void *scales, int64_t ld_scales, void *stream) {
-    if (rows < 0 || cols < 0 || !fmt_ok(fmt) || cols % 32 != 0 || ldx < cols) return MX_ERR_INVALID_ARG;
-    const int64_t cbr = code_bytes(cols, fmt), sbr = cols / 32;
+    const int f = raw(fmt);
+    if (rows < 0 || cols < 0 || !fmt_ok(f) || cols % 32 != 0 || ldx < cols) return MX_ERR_INVALID_ARG;
+    const int64_t cbr = code_bytes(cols, f), sbr = cols / 32;
     if (ld_codes < cbr || ld_scales < sbr) return MX_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0) return MX_OK;
     if (!x_bf16 || !codes || !scales) return MX_ERR_INVALID_ARG;
@@ -258,7 +289,7 @@ mx_status_t mx_quantize_strided(const void *x_bf16, int64_t rows, int64_t cols, 
         return MX_ERR_INVALID_ARG;
     mx_status_t st = check_device();
     if (st != MX_OK) return st;
-    return launched(mx::launch_quantize_rows_strided((const uint16_t *)x_bf16, rows, cols, ldx, fmt, (uint8_t *)codes,
+    return launched(mx::launch_quantize_rows_strided((const uint16_t *)x_bf16, rows, cols, ldx, f, (uint8_t *)codes,
                                                      ld_codes, (uint8_t *)scales, ld_scales, (hipStream_t)stream));
 }
 
