@@ -127,22 +127,29 @@ class Step:
         for ci in CONFIGS:
             cfg = workloads.config(ci)
             tens = {t.name: bf16(cfg, t.name) for t in cfg.tensors}
+            qs = cfg.quants
+            pair = len(qs) == 2 and len({(q.kind, q.fmt, q.sign_mask) for q in qs}) == 1
+            # a transposed pair writes its codes in the K-panel layout, which the GEMM reads in place
+            panels = pair and qs[0].kind != "row" and all(
+                tens[q.tensor].shape[0] % (256 if q.fmt == "e2m1" else 128) == 0 for q in qs)
             ops = {}
             for q in cfg.quants:
                 x = tens[q.tensor]
                 rows, cols = x.shape
                 out_rows, k = (rows, cols) if q.kind == "row" else (cols, rows)
-                codes = torch.empty((out_rows, mx.code_cols(k, q.fmt)), dtype=torch.uint8, device=dev)
+                cshape = ((mx.code_cols(k, q.fmt) // 128, out_rows, 128) if panels
+                          else (out_rows, mx.code_cols(k, q.fmt)))
+                codes = torch.empty(cshape, dtype=torch.uint8, device=dev)
                 scales = torch.empty((out_rows, k // 32), dtype=torch.uint8, device=dev)
                 ops[q.name] = (codes, scales, q.fmt)
-            qs = cfg.quants
-            if len(qs) == 2 and len({(q.kind, q.fmt, q.sign_mask) for q in qs}) == 1:
+            if pair:
                 # both operands of the GEMM in one launch (mx_quantize_pair)
                 q0, q1 = qs
                 x0, x1 = tens[q0.tensor], tens[q1.tensor]
-                fn = (lambda q0=q0, x0=x0, x1=x1, o0=ops[q0.name][:2], o1=ops[q1.name][:2]: mx.quantize_pair(
-                    q0.kind, x0, x1, q0.fmt, q0.sign_mask, out0=o0, out1=o1))
-                self.launches.append(("%s/%s+%s mx_quantize_pair %s %s" % (cfg.name, q0.name, q1.name, q0.kind, q0.fmt),
+                mode = q0.kind + ("_panels" if panels else "")
+                fn = (lambda mode=mode, q0=q0, x0=x0, x1=x1, o0=ops[q0.name][:2], o1=ops[q1.name][:2]:
+                      mx.quantize_pair(mode, x0, x1, q0.fmt, q0.sign_mask, out0=o0, out1=o1))
+                self.launches.append(("%s/%s+%s mx_quantize_pair %s %s" % (cfg.name, q0.name, q1.name, mode, q0.fmt),
                                       "quant", quant_bytes(*x0.shape, q0.fmt) + quant_bytes(*x1.shape, q1.fmt), fn))
             else:
                 for q in qs:
@@ -163,7 +170,8 @@ class Step:
                 fn = (lambda a=a, b=b, out=out: mx.gemm(a[0], a[1], a[2], b[0], b[1], b[2],
                                                         out_dtype=out.dtype, out=out))
                 arith = "fp4" if a[2] == "e2m1" and b[2] == "e2m1" else "bf16"
-                self.launches.append(("%s/%s mx_gemm %sx%s" % (cfg.name, gm.name, a[2], b[2]), "gemm:" + arith,
+                entry = "mx_gemm_layout" if a[0].dim() == 3 or b[0].dim() == 3 else "mx_gemm"
+                self.launches.append(("%s/%s %s %sx%s" % (cfg.name, gm.name, entry, a[2], b[2]), "gemm:" + arith,
                                       2.0 * gm.M * gm.N * gm.K, fn))
         self.flops = sum(w for _, kind, w, _ in self.launches if kind.startswith("gemm"))
 

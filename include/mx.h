@@ -186,16 +186,18 @@ mx_status_t mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int
                              void *scales_t, void *stream);
 
 typedef enum {
-    MX_PAIR_ROW = 0,       /* as mx_quantize                        */
-    MX_PAIR_TRANSPOSE = 1, /* as mx_quantize_transpose              */
-    MX_PAIR_HADAMARD = 2   /* as mx_hadamard32_quantize (sign_mask) */
+    MX_PAIR_ROW = 0,              /* as mx_quantize                               */
+    MX_PAIR_TRANSPOSE = 1,        /* as mx_quantize_transpose                     */
+    MX_PAIR_HADAMARD = 2,         /* as mx_hadamard32_quantize (sign_mask)        */
+    MX_PAIR_TRANSPOSE_PANELS = 3, /* as mx_quantize_transpose_panels              */
+    MX_PAIR_HADAMARD_PANELS = 4   /* as mx_hadamard32_quantize_panels (sign_mask) */
 } mx_pair_mode_t;
 
 /*
  * mx_quantize_pair -- the two operands of one GEMM in one launch.  x0 (rows0
  * x cols0, leading dimension ldx0) goes to codes0 / scales0 and x1 to codes1
  * / scales1, each exactly as the single call of `mode` would quantize it:
- * same format `fmt`, the same sign_mask for MX_PAIR_HADAMARD (ignored
+ * same format `fmt`, the same sign_mask for the rotated modes (ignored
  * otherwise), and per tensor the sizes, layouts, rules and errors of that
  * call.  The GEMMs of a linear layer take both operands in the same form
  * (FP4-training article on hzrcw.cc, section 02: Fprop X and W in row mode,
@@ -282,6 +284,53 @@ mx_status_t mx_quantize_strided(const void *x_bf16, int64_t rows, int64_t cols, 
 mx_status_t mx_gemm_strided(const void *a_codes, int64_t lda, const void *a_scales, int64_t ldsa, mx_format_t fa,
                             const void *b_codes, int64_t ldb, const void *b_scales, int64_t ldsb, mx_format_t fb,
                             int64_t M, int64_t N, int64_t K, void *c, mx_out_t out, int64_t ldc, void *stream);
+
+/*
+ * K-panel layout of MX codes -- an alternative storage order of the same
+ * codes, chosen by the library for its own transposed quantizers and GEMM
+ * (no page prescribes a layout).  The codes of R rows of K elements are K / P
+ * panels of R rows x 128 bytes, P = 256 elements for E2M1 and 128 for
+ * E4M3 / E5M2: code byte j (j < 128) of row r in panel p is at
+ * codes + p * (R * 128) + r * 128 + j, i.e. bytes [128 p, 128 p + 128) of the
+ * dense row r.  Same total size as the dense layout; scales stay dense
+ * ([R x K/32]).  A transposed quantizer writes each workgroup's codes as
+ * whole 32 KiB runs in this order (256 runs of 128 bytes in the dense one),
+ * and the GEMM reads both layouts at about the same speed.
+ */
+typedef enum {
+    MX_LAYOUT_ROWS = 0,   /* dense row-major codes, as every other call */
+    MX_LAYOUT_PANELS = 1  /* K-panel layout above                        */
+} mx_layout_t;
+
+/*
+ * mx_quantize_transpose_panels, mx_hadamard32_quantize_panels -- as
+ * mx_quantize_transpose and mx_hadamard32_quantize (same codes and scales,
+ * same errors), with the codes in the K-panel layout (R = cols output rows,
+ * K = rows).  rows must also be a multiple of the panel width: 256 for E2M1,
+ * 128 for E4M3 / E5M2 (else MX_ERR_INVALID_ARG).  For callers: the
+ * weight-gradient operands that mx_gemm_layout then reads in place.
+ */
+mx_status_t mx_quantize_transpose_panels(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                                         mx_format_t fmt, void *codes, void *scales, void *stream);
+mx_status_t mx_hadamard32_quantize_panels(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                                          uint32_t sign_mask, mx_format_t fmt, void *codes, void *scales,
+                                          void *stream);
+
+/*
+ * mx_gemm_layout -- mx_gemm with each operand's codes in the layout given
+ * (a_layout, b_layout); scales dense.  With both MX_LAYOUT_ROWS it is
+ * mx_gemm.  A K-panel operand needs the pipelined kernel: K a multiple of
+ * 512, 16-byte aligned code and dword-aligned scale pointers, the operand's
+ * code bytes below 2^31, and, for an E2M1 operand, an E2M1 partner (beside
+ * an FP8 operand an E2M1 stage row is 64 bytes, half a panel row); otherwise
+ * MX_ERR_UNSUPPORTED.  Any M and N.  Same computation as mx_gemm: on the
+ * same values the results are bit-identical to mx_gemm's with dense
+ * operands.  Errors otherwise as mx_gemm (MX_ERR_INVALID_ARG for an unknown
+ * layout).
+ */
+mx_status_t mx_gemm_layout(const void *a_codes, mx_layout_t a_layout, const void *a_scales, mx_format_t fa,
+                           const void *b_codes, mx_layout_t b_layout, const void *b_scales, mx_format_t fb,
+                           int64_t M, int64_t N, int64_t K, void *c, mx_out_t out, int64_t ldc, void *stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char *mx_status_string(mx_status_t s);

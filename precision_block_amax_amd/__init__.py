@@ -61,9 +61,13 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
         L.mx_quantize_strided.argtypes = [P, i64, i64, i64, i32, P, i64, P, i64, P]
         L.mx_gemm_strided.argtypes = [P, i64, P, i64, i32, P, i64, P, i64, i32, i64, i64, i64, P, i32, i64, P]
+        L.mx_quantize_transpose_panels.argtypes = [P, i64, i64, i64, i32, P, P, P]
+        L.mx_hadamard32_quantize_panels.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
+        L.mx_gemm_layout.argtypes = [P, i32, P, i32, P, i32, P, i32, i64, i64, i64, P, i32, i64, P]
         for fn in (L.mx_quantize, L.mx_quantize_transpose, L.mx_hadamard32_quantize, L.mx_quantize_dual,
                    L.mx_quantize_transpose_sr, L.mx_quantize_pair, L.mx_gemm, L.mx_quantize_strided,
-                   L.mx_gemm_strided):
+                   L.mx_gemm_strided, L.mx_quantize_transpose_panels, L.mx_hadamard32_quantize_panels,
+                   L.mx_gemm_layout):
             fn.restype = ctypes.c_int
         L.mx_status_string.argtypes = [ctypes.c_int]
         L.mx_status_string.restype = ctypes.c_char_p
@@ -106,8 +110,10 @@ def _check_bf16_2d(x: torch.Tensor) -> None:
         raise ValueError("the last dimension must be contiguous")
 
 
-def _outputs(device, rows_out: int, k: int, fmt: int, out) -> Tuple[torch.Tensor, torch.Tensor]:
+def _outputs(device, rows_out: int, k: int, fmt: int, out, panels: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     shape_c, shape_s = (rows_out, code_cols(k, fmt)), (rows_out, k // 32)
+    if panels:  # K-panel layout: [K panels x rows x 128 bytes]
+        shape_c = (code_cols(k, fmt) // 128, rows_out, 128)
     if out is None:
         return (torch.empty(shape_c, dtype=torch.uint8, device=device),
                 torch.empty(shape_s, dtype=torch.uint8, device=device))
@@ -185,14 +191,25 @@ def fsdp_payload(w_rows: torch.Tensor, fmt, out: Optional[torch.Tensor] = None,
     return out
 
 
-def quantize_transpose(x: torch.Tensor, fmt, out=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """mx_quantize_transpose: blocks of 32 along dim 0; codes [C x R(/2)], scales [C x R/32]"""
+_LAYOUTS = ("rows", "panels")
+
+
+def _panels(layout: str) -> bool:
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be one of %s" % (_LAYOUTS,))
+    return layout == "panels"
+
+
+def quantize_transpose(x: torch.Tensor, fmt, out=None, stream=None, layout: str = "rows") -> Tuple[torch.Tensor, torch.Tensor]:
+    """mx_quantize_transpose: blocks of 32 along dim 0; codes [C x R(/2)], scales [C x R/32].
+    layout="panels": mx_quantize_transpose_panels, codes [R(/2) / 128 x C x 128] (K-panel layout)"""
     _check_bf16_2d(x)
     f = _fmt(fmt)
     rows, cols = x.shape
-    codes, scales = _outputs(x.device, cols, rows, f, out)
-    _check(lib().mx_quantize_transpose(_ptr(x), rows, cols, _ldx(x), f, _ptr(codes), _ptr(scales),
-                                       _stream(x.device, stream)))
+    pan = _panels(layout)
+    codes, scales = _outputs(x.device, cols, rows, f, out, pan)
+    fn = lib().mx_quantize_transpose_panels if pan else lib().mx_quantize_transpose
+    _check(fn(_ptr(x), rows, cols, _ldx(x), f, _ptr(codes), _ptr(scales), _stream(x.device, stream)))
     return codes, scales
 
 
@@ -212,14 +229,17 @@ def quantize_dual(x: torch.Tensor, fmt_row, fmt_t, rotate: bool = False, sign_ma
 
 
 def hadamard32_quantize(x: torch.Tensor, fmt, sign_mask: int = 0, out=None,
-                        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """mx_hadamard32_quantize: rotate each 32-row block, then transposed-mode quantize"""
+                        stream=None, layout: str = "rows") -> Tuple[torch.Tensor, torch.Tensor]:
+    """mx_hadamard32_quantize: rotate each 32-row block, then transposed-mode quantize
+    (layout="panels": mx_hadamard32_quantize_panels, codes in the K-panel layout)"""
     _check_bf16_2d(x)
     f = _fmt(fmt)
     rows, cols = x.shape
-    codes, scales = _outputs(x.device, cols, rows, f, out)
-    _check(lib().mx_hadamard32_quantize(_ptr(x), rows, cols, _ldx(x), sign_mask & 0xFFFFFFFF, f,
-                                        _ptr(codes), _ptr(scales), _stream(x.device, stream)))
+    pan = _panels(layout)
+    codes, scales = _outputs(x.device, cols, rows, f, out, pan)
+    fn = lib().mx_hadamard32_quantize_panels if pan else lib().mx_hadamard32_quantize
+    _check(fn(_ptr(x), rows, cols, _ldx(x), sign_mask & 0xFFFFFFFF, f, _ptr(codes), _ptr(scales),
+              _stream(x.device, stream)))
     return codes, scales
 
 
@@ -237,14 +257,15 @@ def quantize_transpose_sr(x: torch.Tensor, fmt, seed: int, rotate: bool = False,
     return codes, scales
 
 
-_PAIR_MODES = {"row": 0, "transpose": 1, "hadamard": 2}
+_PAIR_MODES = {"row": 0, "transpose": 1, "hadamard": 2, "transpose_panels": 3, "hadamard_panels": 4}
 
 
 def quantize_pair(mode: str, x0: torch.Tensor, x1: torch.Tensor, fmt, sign_mask: int = 0, out0=None, out1=None,
                   stream=None):
     """mx_quantize_pair: both operands of a GEMM in one launch, each exactly as quantize
     (mode "row"), quantize_transpose ("transpose") or hadamard32_quantize ("hadamard", with
-    sign_mask) would quantize it.  Returns ((codes0, scales0), (codes1, scales1))."""
+    sign_mask) would quantize it; "transpose_panels" and "hadamard_panels" write the codes in
+    the K-panel layout (layout="panels").  Returns ((codes0, scales0), (codes1, scales1))."""
     if mode not in _PAIR_MODES:
         raise ValueError("mode must be one of %s" % sorted(_PAIR_MODES))
     _check_bf16_2d(x0)
@@ -255,7 +276,8 @@ def quantize_pair(mode: str, x0: torch.Tensor, x1: torch.Tensor, fmt, sign_mask:
     outs = []
     for x, out in ((x0, out0), (x1, out1)):
         rows, cols = x.shape
-        outs.append(_outputs(x.device, rows, cols, f, out) if mode == "row" else _outputs(x.device, cols, rows, f, out))
+        outs.append(_outputs(x.device, rows, cols, f, out) if mode == "row" else
+                    _outputs(x.device, cols, rows, f, out, mode.endswith("_panels")))
     (c0, s0), (c1, s1) = outs
     _check(lib().mx_quantize_pair(_PAIR_MODES[mode], f, sign_mask & 0xFFFFFFFF,
                                   _ptr(x0), x0.shape[0], x0.shape[1], _ldx(x0), _ptr(c0), _ptr(s0),
@@ -269,7 +291,9 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, fa, b_codes: torch.Tenso
          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """mx_gemm: C[M x N] = A[M x K] . B[N x K]^T on MX operands.  Operands may be
     row-strided uint8 views (rows contiguous), e.g. payload_views() of a gathered
-    FSDP2 payload; those go through mx_gemm_strided."""
+    FSDP2 payload; those go through mx_gemm_strided.  Codes in the K-panel layout
+    (3-D, [K bytes / 128 x rows x 128], as quantize_transpose(layout="panels")
+    writes them) go through mx_gemm_layout."""
     fa_, fb_ = _fmt(fa), _fmt(fb)
     M, kb = a_scales.shape
     N, kb2 = b_scales.shape
@@ -279,8 +303,18 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, fa, b_codes: torch.Tenso
     dev = a_codes.device
     if not a_codes.is_cuda:
         raise ValueError("operands must be on a GPU")
-    lds = [_row_strided(t, shp, dev) for t, shp in ((a_codes, (M, code_cols(K, fa_))), (a_scales, (M, kb)),
-                                                     (b_codes, (N, code_cols(K, fb_))), (b_scales, (N, kb)))]
+    panel = [t.dim() == 3 for t in (a_codes, b_codes)]
+    if any(panel):
+        for t, rows, f, pn in ((a_codes, M, fa_, panel[0]), (b_codes, N, fb_, panel[1])):
+            shp = (code_cols(K, f) // 128, rows, 128) if pn else (rows, code_cols(K, f))
+            if t.dtype != torch.uint8 or tuple(t.shape) != shp or t.device != dev or not t.is_contiguous():
+                raise ValueError("expected a contiguous uint8 tensor of shape %s on %s" % (shp, dev))
+        for t, shp in ((a_scales, (M, kb)), (b_scales, (N, kb))):
+            if t.dtype != torch.uint8 or tuple(t.shape) != shp or t.device != dev or not t.is_contiguous():
+                raise ValueError("expected a contiguous uint8 tensor of shape %s on %s" % (shp, dev))
+    else:
+        lds = [_row_strided(t, shp, dev) for t, shp in ((a_codes, (M, code_cols(K, fa_))), (a_scales, (M, kb)),
+                                                         (b_codes, (N, code_cols(K, fb_))), (b_scales, (N, kb)))]
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be float32 or bfloat16")
     if out is None:
@@ -289,7 +323,10 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, fa, b_codes: torch.Tenso
         raise ValueError("bad output buffer")
     ldc = out.stride(0) if M > 1 else N
     o = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
-    if all(t.is_contiguous() for t in (a_codes, a_scales, b_codes, b_scales)):
+    if any(panel):
+        _check(lib().mx_gemm_layout(_ptr(a_codes), int(panel[0]), _ptr(a_scales), fa_, _ptr(b_codes), int(panel[1]),
+                                    _ptr(b_scales), fb_, M, N, K, _ptr(out), o, ldc, _stream(dev, stream)))
+    elif all(t.is_contiguous() for t in (a_codes, a_scales, b_codes, b_scales)):
         _check(lib().mx_gemm(_ptr(a_codes), _ptr(a_scales), fa_, _ptr(b_codes), _ptr(b_scales), fb_,
                              M, N, K, _ptr(out), o, ldc, _stream(dev, stream)))
     else:

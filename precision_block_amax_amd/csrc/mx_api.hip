@@ -33,6 +33,9 @@ bool fmt_ok(int f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; }
 
 int64_t code_bytes(int64_t n, int fmt) { return fmt == MX_E2M1 ? n / 2 : n; }
 
+// K-panel width in elements: 128 code bytes
+int64_t panel_elems(int fmt) { return fmt == MX_E2M1 ? 256 : 128; }
+
 // half-open byte ranges [p, p + n) overlap
 bool overlap(const void *p, int64_t n, const void *q, int64_t m) {
     if (n <= 0 || m <= 0) return false;
@@ -128,14 +131,27 @@ mx_status_t check_gemm(const void *a_codes, int64_t lda, const void *a_scales, i
 // mx_gemm_strided with its enum arguments already read as ints
 mx_status_t gemm_strided(const void *a_codes, int64_t lda, const void *a_scales, int64_t ldsa, int fa,
                          const void *b_codes, int64_t ldb, const void *b_scales, int64_t ldsb, int fb, int64_t M,
-                         int64_t N, int64_t K, void *c, int out, int64_t ldc, void *stream) {
+                         int64_t N, int64_t K, void *c, int out, int64_t ldc, void *stream, int64_t kpa = 0,
+                         int64_t kpb = 0) {
     mx_status_t st = check_gemm(a_codes, lda, a_scales, ldsa, fa, b_codes, ldb, b_scales, ldsb, fb, M, N, K, c, out,
                                 ldc);
     if (st != MX_OK || M == 0 || N == 0) return st;
     if ((st = check_device()) != MX_OK) return st;
     return launched(mx::launch_gemm((const uint8_t *)a_codes, lda, (const uint8_t *)a_scales, ldsa, fa,
                                     (const uint8_t *)b_codes, ldb, (const uint8_t *)b_scales, ldsb, fb, M, N, K, c,
-                                    out == MX_OUT_BF16, ldc, (hipStream_t)stream));
+                                    out == MX_OUT_BF16, ldc, (hipStream_t)stream, kpa, kpb));
+}
+
+// the transposed quantizers with K-panel code output
+mx_status_t quantize_transpose_panels(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, int f,
+                                      bool rotate, uint32_t sign_mask, void *codes, void *scales, void *stream) {
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, f, codes, scales, true);
+    if (st != MX_OK) return st;
+    if (rows % panel_elems(f) != 0) return MX_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return MX_OK;
+    if ((st = check_device()) != MX_OK) return st;
+    return launched(mx::launch_quantize_transpose((const uint16_t *)x_bf16, rows, cols, ldx, f, rotate, sign_mask,
+                                                  (uint8_t *)codes, (uint8_t *)scales, (hipStream_t)stream, true));
 }
 
 }  // namespace
@@ -186,6 +202,17 @@ mx_status_t mx_hadamard32_quantize(const void *x_bf16, int64_t rows, int64_t col
                                                   (hipStream_t)stream));
 }
 
+mx_status_t mx_quantize_transpose_panels(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                                         mx_format_t fmt, void *codes, void *scales, void *stream) {
+    return quantize_transpose_panels(x_bf16, rows, cols, ldx, raw(fmt), false, 0u, codes, scales, stream);
+}
+
+mx_status_t mx_hadamard32_quantize_panels(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                                          uint32_t sign_mask, mx_format_t fmt, void *codes, void *scales,
+                                          void *stream) {
+    return quantize_transpose_panels(x_bf16, rows, cols, ldx, raw(fmt), true, sign_mask, codes, scales, stream);
+}
+
 mx_status_t mx_quantize_transpose_sr(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, int rotate,
                                      uint32_t sign_mask, uint64_t seed, mx_format_t fmt, void *codes, void *scales,
                                      void *stream) {
@@ -225,8 +252,14 @@ mx_status_t mx_quantize_pair(mx_pair_mode_t mode, mx_format_t fmt, uint32_t sign
                              int64_t rows1, int64_t cols1, int64_t ldx1, void *codes1, void *scales1, void *stream) {
     const int m = raw(mode);
     const int f = raw(fmt);
-    if (m != MX_PAIR_ROW && m != MX_PAIR_TRANSPOSE && m != MX_PAIR_HADAMARD) return MX_ERR_INVALID_ARG;
+    if (m != MX_PAIR_ROW && m != MX_PAIR_TRANSPOSE && m != MX_PAIR_HADAMARD && m != MX_PAIR_TRANSPOSE_PANELS &&
+        m != MX_PAIR_HADAMARD_PANELS)
+        return MX_ERR_INVALID_ARG;
     const bool tr = m != MX_PAIR_ROW;
+    const bool panels = m == MX_PAIR_TRANSPOSE_PANELS || m == MX_PAIR_HADAMARD_PANELS;
+    const bool rot = m == MX_PAIR_HADAMARD || m == MX_PAIR_HADAMARD_PANELS;
+    if (panels && fmt_ok(f) && (rows0 % panel_elems(f) != 0 || rows1 % panel_elems(f) != 0))
+        return MX_ERR_INVALID_ARG;
     mx_status_t st = check_quant(x0, rows0, cols0, ldx0, f, codes0, scales0, tr);
     if (st != MX_OK) return st;
     if ((st = check_quant(x1, rows1, cols1, ldx1, f, codes1, scales1, tr)) != MX_OK) return st;
@@ -249,10 +282,10 @@ mx_status_t mx_quantize_pair(mx_pair_mode_t mode, mx_format_t fmt, uint32_t sign
     if (e0 || e1) {  // one tensor: the single call
         const mx::QuantJob &j = e0 ? j1 : j0;
         if (!tr) return launched(mx::launch_quantize_rows(j.x, j.rows, j.cols, j.ldx, f, j.codes, j.scales, s));
-        return launched(mx::launch_quantize_transpose(j.x, j.rows, j.cols, j.ldx, f, m == MX_PAIR_HADAMARD,
-                                                      sign_mask, j.codes, j.scales, s));
+        return launched(mx::launch_quantize_transpose(j.x, j.rows, j.cols, j.ldx, f, rot, rot ? sign_mask : 0u,
+                                                      j.codes, j.scales, s, panels));
     }
-    return launched(mx::launch_quantize_pair((int)m, f, m == MX_PAIR_HADAMARD ? sign_mask : 0u, j0, j1, s));
+    return launched(mx::launch_quantize_pair(m, f, rot ? sign_mask : 0u, j0, j1, s));
 }
 
 mx_status_t mx_gemm(const void *a_codes, const void *a_scales, mx_format_t fa, const void *b_codes,
@@ -269,6 +302,37 @@ mx_status_t mx_gemm_strided(const void *a_codes, int64_t lda, const void *a_scal
                             int64_t M, int64_t N, int64_t K, void *c, mx_out_t out, int64_t ldc, void *stream) {
     return gemm_strided(a_codes, lda, a_scales, ldsa, raw(fa), b_codes, ldb, b_scales, ldsb, raw(fb), M, N, K, c,
                         raw(out), ldc, stream);
+}
+
+mx_status_t mx_gemm_layout(const void *a_codes, mx_layout_t a_layout, const void *a_scales, mx_format_t fa,
+                           const void *b_codes, mx_layout_t b_layout, const void *b_scales, mx_format_t fb,
+                           int64_t M, int64_t N, int64_t K, void *c, mx_out_t out, int64_t ldc, void *stream) {
+    const int a = raw(fa), b = raw(fb), la = raw(a_layout), lb = raw(b_layout);
+    if (!fmt_ok(a) || !fmt_ok(b) || K < 0 || (la != MX_LAYOUT_ROWS && la != MX_LAYOUT_PANELS) ||
+        (lb != MX_LAYOUT_ROWS && lb != MX_LAYOUT_PANELS))
+        return MX_ERR_INVALID_ARG;
+    const int64_t lda = code_bytes(K, a), ldb = code_bytes(K, b);
+    int64_t kpa = 0, kpb = 0;
+    if (la == MX_LAYOUT_PANELS || lb == MX_LAYOUT_PANELS) {
+        // the argument checks of mx_gemm first (their errors take precedence)
+        mx_status_t st = check_gemm(a_codes, lda, a_scales, K / 32, a, b_codes, ldb, b_scales, K / 32, b, M, N, K, c,
+                                    raw(out), ldc);
+        if (st != MX_OK || M == 0 || N == 0) return st;
+        const bool fp4 = a == MX_E2M1 && b == MX_E2M1;
+        const bool aligned = ((uintptr_t)a_codes % 16 == 0) && ((uintptr_t)b_codes % 16 == 0) &&
+                             ((uintptr_t)a_scales % 4 == 0) && ((uintptr_t)b_scales % 4 == 0);
+        if (K % 512 != 0 || !aligned) return MX_ERR_UNSUPPORTED;
+        if (la == MX_LAYOUT_PANELS) {
+            if ((a == MX_E2M1 && !fp4) || M * lda >= ((int64_t)1 << 31)) return MX_ERR_UNSUPPORTED;
+            kpa = M * 128;
+        }
+        if (lb == MX_LAYOUT_PANELS) {
+            if ((b == MX_E2M1 && !fp4) || N * ldb >= ((int64_t)1 << 31)) return MX_ERR_UNSUPPORTED;
+            kpb = N * 128;
+        }
+    }
+    return gemm_strided(a_codes, lda, a_scales, K / 32, a, b_codes, ldb, b_scales, K / 32, b, M, N, K, c, raw(out),
+                        ldc, stream, kpa, kpb);
 }
 
 mx_status_t mx_quantize_strided(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt,

@@ -13,7 +13,7 @@ MX_PAIR(2, 0) MX_PAIR(2, 1) MX_PAIR(2, 2)
 
 hipError_t launch_gemm(const uint8_t *a, int64_t lda, const uint8_t *as, int64_t ldsa, int fa, const uint8_t *b,
                        int64_t ldb, const uint8_t *bs, int64_t ldsb, int fb, int64_t M, int64_t N, int64_t K, void *c,
-                       bool bf16_out, int64_t ldc, hipStream_t stream) {
+                       bool bf16_out, int64_t ldc, hipStream_t stream, int64_t kpa, int64_t kpb) {
     if (K == 0) {
         const int64_t n = M * N;
         const dim3 grid((unsigned)((n + 255) / 256));
@@ -26,6 +26,7 @@ hipError_t launch_gemm(const uint8_t *a, int64_t lda, const uint8_t *as, int64_t
     GemmArgs g;
     g.a = a; g.as = as; g.b = b; g.bs = bs; g.c = c; g.ldc = ldc;
     g.lda = lda; g.ldsa = ldsa; g.ldb = ldb; g.ldsb = ldsb;
+    g.kpa = kpa; g.kpb = kpb;
     g.M = (int)M; g.N = (int)N; g.K = (int)K;
     g.tiles_m = (int)((M + BM - 1) / BM);
     g.tiles_n = (int)((N + BN - 1) / BN);

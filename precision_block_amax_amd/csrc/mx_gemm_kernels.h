@@ -62,6 +62,10 @@ struct GemmArgs {
     void *c;
     int64_t ldc;
     int64_t lda, ldsa, ldb, ldsb;
+    // K-panel layout of an operand's codes (pipelined kernels only): the 128
+    // code bytes of row r that one stage reads, for K panel p, sit at
+    // p * kp + r * 128; kp = 0 is the row layout above
+    int64_t kpa = 0, kpb = 0;
     int M, N, K;
     int tiles_m, tiles_n;
 };
@@ -641,14 +645,17 @@ __device__ __forceinline__ void row_scale_range(const uint8_t *p, int n, bool ve
 
 // true if every block of the row whose scale byte is 0 holds only zero codes
 // (either sign: MAG masks the magnitude bits): codes c of the row (16-byte
-// aligned), scales p, n blocks of BB code bytes
+// aligned; with kp != 0 the row's bytes of K panel 0, see GemmArgs), scales p,
+// n blocks of BB code bytes
 template <int BB, uint32_t MAG>
-__device__ __forceinline__ bool zero_blocks_clear(const uint8_t *c, const uint8_t *p, int n, bool vec) {
+__device__ __forceinline__ bool zero_blocks_clear(const uint8_t *c, const uint8_t *p, int n, bool vec, int64_t kp) {
     uint32_t any = 0;
     const auto check = [&](int k) {
+        const int64_t pos = (int64_t)k * BB;
+        const uint8_t *blk = kp ? c + (pos >> 7) * kp + (pos & 127) : c + pos;
 #pragma unroll
         for (int q = 0; q < BB; q += 16) {
-            const uint4 t = *reinterpret_cast<const uint4 *>(c + (int64_t)k * BB + q);
+            const uint4 t = *reinterpret_cast<const uint4 *>(blk + q);
             any |= (t.x | t.y | t.z | t.w) & MAG;
         }
     };
@@ -737,12 +744,18 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     // order of the fp32 sum over K changes.
     const bool krev = ((blockIdx.x >> 3) / kCusPerXcd) & 1;
 
-    // row strides in bytes (the launcher keeps 256 rows of either operand below 2^31 bytes)
-    const int rowA = (int)g.lda, rowB = (int)g.ldb, srowA = (int)g.ldsa, srowB = (int)g.ldsb;
+    // row strides in bytes (the launcher keeps 256 rows of either operand below 2^31 bytes);
+    // a K-panel operand has rows of one stage's RB = 128 bytes, and stage kt in panel kt
+    const int rowA = g.kpa ? RBA : (int)g.lda, rowB = g.kpb ? RBB : (int)g.ldb;
+    const int srowA = (int)g.ldsa, srowB = (int)g.ldsb;
     const int kblocks = g.K / 32;
     const int ntk = g.K / KE;
     const int mrows = min(BM, g.M - m0), nrows = min(BN, g.N - n0);
-    const uint32_t nrecA = (uint32_t)mrows * rowA, nrecB = (uint32_t)nrows * rowB;
+    // a K-panel operand's record range runs to the end of its codes (rows past M in a panel
+    // are the next panel's first rows: they only reach rows of C past M, which are not stored)
+    const uint32_t nrecA = g.kpa ? (uint32_t)((int64_t)ntk * g.kpa - (int64_t)m0 * RBA) : (uint32_t)mrows * rowA;
+    const uint32_t nrecB = g.kpb ? (uint32_t)((int64_t)ntk * g.kpb - (int64_t)n0 * RBB) : (uint32_t)nrows * rowB;
+    const int stA_ = g.kpa ? (int)g.kpa : RBA, stB_ = g.kpb ? (int)g.kpb : RBB;  // bytes per stage
     const uint32_t nrecSA = (uint32_t)mrows * srowA, nrecSB = (uint32_t)nrows * srowB;
     const v4i rA = rsrc(g.a + (int64_t)m0 * rowA, nrecA);
     const v4i rB = rsrc(g.b + (int64_t)n0 * rowB, nrecB);
@@ -780,8 +793,9 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
             // R <= 127.  Then the tile keeps the fast path; a block of genuinely tiny
             // values (nonzero codes under scale byte 0) sends it to the exact kernel.
             const uint8_t *pc = isA ? g.a + (int64_t)gr * rowA : g.b + (int64_t)gr * rowB;
-            w = mx_ > 127 || !((isA ? A4 : B4) ? zero_blocks_clear<16, 0x77777777u>(pc, ps, kblocks, vec)
-                                                : zero_blocks_clear<32, 0x7F7F7F7Fu>(pc, ps, kblocks, vec));
+            const int64_t kp = isA ? g.kpa : g.kpb;
+            w = mx_ > 127 || !((isA ? A4 : B4) ? zero_blocks_clear<16, 0x77777777u>(pc, ps, kblocks, vec, kp)
+                                                : zero_blocks_clear<32, 0x7F7F7F7Fu>(pc, ps, kblocks, vec, kp));
         }
         if (__syncthreads_or(w) != 0) {  // uniform across the workgroup
             if (tid == 0) mark_tile<BF16OUT>(g, m0, n0);
@@ -821,7 +835,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     auto issue = [&](auto S, auto T, auto SCALES, int kt) {
         const bool live = kt < ntk;
         const int pk = krev ? (ntk - SPS - kt / SPS * SPS + kt % SPS) : kt;  // stage of K loaded
-        const int soA = live ? pk * RBA : (int)nrecA, soB = live ? pk * RBB : (int)nrecB;
+        const int soA = live ? pk * stA_ : (int)nrecA, soB = live ? pk * stB_ : (int)nrecB;
 #pragma unroll
         for (int q = 0; q < NIA; q++)
             dma16(rA, stA(S) + (dw * NIA + q) * 1024, (q & 1) ? voffA1 : voffA, soA + q * (64 / CPRA) * rowA);
@@ -1169,6 +1183,16 @@ hipError_t launch_fmt(const GemmArgs &g, bool bf16, hipStream_t stream) {
                            ((uintptr_t)g.as % 4 == 0) && ((uintptr_t)g.bs % 4 == 0) &&
                            g.lda % 16 == 0 && g.ldb % 16 == 0 && g.ldsa % 16 == 0 && g.ldsb % 16 == 0 &&
                            (int64_t)BM * ldmax < ((int64_t)1 << 31) && (int64_t)BM * ldsmax < ((int64_t)1 << 31);
+    if (g.kpa || g.kpb) {
+        // K-panel operands: the pipelined kernels only, with 128-byte stage rows (E2M1 beside
+        // E2M1, or FP8), and every panel offset in 31 bits
+        constexpr int KE = fp4 ? 256 : 128;
+        constexpr int RBA = FA == E2M1 ? KE / 2 : KE, RBB = FB == E2M1 ? KE / 2 : KE;
+        const int64_t ntk = g.K / KE;
+        if (!pipelined || (g.kpa && (RBA != 128 || ntk * g.kpa >= ((int64_t)1 << 31))) ||
+            (g.kpb && (RBB != 128 || ntk * g.kpb >= ((int64_t)1 << 31))))
+            return hipErrorInvalidValue;
+    }
     if (pipelined) {
         const dim3 block(pipe::PNT);
         if constexpr (fp4) {

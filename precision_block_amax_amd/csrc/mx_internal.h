@@ -37,7 +37,7 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, i
                                 uint8_t *codes, uint8_t *scales, hipStream_t stream);
 hipError_t launch_quantize_transpose(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
                                      int fmt, bool rotate, uint32_t sign_mask, uint8_t *codes,
-                                     uint8_t *scales, hipStream_t stream);
+                                     uint8_t *scales, hipStream_t stream, bool panels = false);
 
 // transposed mode (rotated or not) with stochastic rounding under `seed`
 hipError_t launch_quantize_transpose_sr(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
@@ -56,15 +56,18 @@ struct QuantJob {
     uint8_t *codes, *scales;
 };
 
-// Both tensors in one launch (mode 0: row, 1: transposed, 2: rotated transposed), or
-// two launches where they need different kernel variants.  Both non-empty.
+// Both tensors in one launch (mode 0: row, 1: transposed, 2: rotated transposed, 3 and 4:
+// modes 1 and 2 with K-panel code output), or two launches where they need different
+// kernel variants.  Both non-empty.
 hipError_t launch_quantize_pair(int mode, int fmt, uint32_t sign_mask, const QuantJob &a, const QuantJob &b,
                                 hipStream_t stream);
 
-// GEMM launcher (mx_gemm.hip); operand row strides in bytes (codes, scales).
+// GEMM launcher (mx_gemm.hip); operand row strides in bytes (codes, scales);
+// kpa / kpb != 0: that operand's codes are K-panel-major with this panel
+// stride in bytes (GemmArgs).
 hipError_t launch_gemm(const uint8_t *a, int64_t lda, const uint8_t *as, int64_t ldsa, int fa, const uint8_t *b,
                        int64_t ldb, const uint8_t *bs, int64_t ldsb, int fb, int64_t M, int64_t N, int64_t K, void *c,
-                       bool bf16_out, int64_t ldc, hipStream_t stream);
+                       bool bf16_out, int64_t ldc, hipStream_t stream, int64_t kpa = 0, int64_t kpb = 0);
 
 // Row mode with strided outputs: row r's codes at codes + r * ld_codes, its
 // scales at scales + r * ld_scales (bytes).

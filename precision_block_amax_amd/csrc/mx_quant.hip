@@ -76,17 +76,19 @@ hipError_t launch_rows_strided_fmt(const uint16_t *x, int64_t rows, int64_t cols
 
 template <int F, bool ROTATE>
 hipError_t launch_tr_fmt(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, uint32_t mask,
-                         uint8_t *codes, uint8_t *scales, hipStream_t stream) {
+                         uint8_t *codes, uint8_t *scales, hipStream_t stream, bool panels = false) {
     const bool vec = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0) && ((uintptr_t)codes % 16 == 0);
     const unsigned tx = (unsigned)((cols + kTrCols - 1) / kTrCols);
     if (vec) {
         constexpr int W = tr_waves<F, true, -1, false>();
         hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true>), dim3(tx, (unsigned)((rows / 32 + W - 1) / W)),
-                           dim3(64 * W), 0, stream, x, ldx, rows, cols, mask, codes, scales);
+                           dim3(64 * W), 0, stream, x, ldx, rows, cols, mask, codes, scales, nullptr, nullptr,
+                           (uint64_t)0, nullptr, 0, 0, 0, nullptr, nullptr, 0u, panels ? 1 : 0);
     } else {
         constexpr int W = tr_waves<F, false, -1, false>();
         hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, false>), dim3(tx, (unsigned)((rows / 32 + W - 1) / W)),
-                           dim3(64 * W), 0, stream, x, ldx, rows, cols, mask, codes, scales);
+                           dim3(64 * W), 0, stream, x, ldx, rows, cols, mask, codes, scales, nullptr, nullptr,
+                           (uint64_t)0, nullptr, 0, 0, 0, nullptr, nullptr, 0u, panels ? 1 : 0);
     }
     return hipGetLastError();
 }
@@ -134,13 +136,17 @@ hipError_t launch_rows_pair_fmt(const QuantJob &a, const QuantJob &b, hipStream_
 }
 
 template <int F, bool ROTATE>
-hipError_t launch_tr_pair_fmt(const QuantJob &a, const QuantJob &b, uint32_t mask, hipStream_t stream) {
+hipError_t launch_tr_pair_fmt(const QuantJob &a, const QuantJob &b, uint32_t mask, hipStream_t stream,
+                              bool panels) {
     auto vec = [](const QuantJob &j) {
         return ((uintptr_t)j.x % 8 == 0) && (j.ldx % 4 == 0) && ((uintptr_t)j.codes % 16 == 0);
     };
     if (!vec(a) || !vec(b)) {
-        const hipError_t e = launch_tr_fmt<F, ROTATE>(a.x, a.rows, a.cols, a.ldx, mask, a.codes, a.scales, stream);
-        return e != hipSuccess ? e : launch_tr_fmt<F, ROTATE>(b.x, b.rows, b.cols, b.ldx, mask, b.codes, b.scales, stream);
+        const hipError_t e =
+            launch_tr_fmt<F, ROTATE>(a.x, a.rows, a.cols, a.ldx, mask, a.codes, a.scales, stream, panels);
+        return e != hipSuccess
+                   ? e
+                   : launch_tr_fmt<F, ROTATE>(b.x, b.rows, b.cols, b.ldx, mask, b.codes, b.scales, stream, panels);
     }
     const uint32_t tx = (uint32_t)((a.cols + kTrCols - 1) / kTrCols), ux = (uint32_t)((b.cols + kTrCols - 1) / kTrCols);
     constexpr int W = tr_waves<F, true, -1, false>();
@@ -148,7 +154,7 @@ hipError_t launch_tr_pair_fmt(const QuantJob &a, const QuantJob &b, uint32_t mas
     const dim3 grid(tx + ux, (unsigned)(ra > rb ? ra : rb));
     hipLaunchKernelGGL((k_quantize_transpose<F, ROTATE, true, -1, false, true>), grid, dim3(64 * W), 0, stream,
                        a.x, a.ldx, a.rows, a.cols, mask, a.codes, a.scales, nullptr, nullptr, (uint64_t)0,
-                       b.x, b.ldx, b.rows, b.cols, b.codes, b.scales, tx);
+                       b.x, b.ldx, b.rows, b.cols, b.codes, b.scales, tx, panels ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -192,18 +198,18 @@ hipError_t launch_quantize_rows_strided(const uint16_t *x, int64_t rows, int64_t
 
 hipError_t launch_quantize_transpose(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
                                      int fmt, bool rotate, uint32_t sign_mask, uint8_t *codes,
-                                     uint8_t *scales, hipStream_t stream) {
+                                     uint8_t *scales, hipStream_t stream, bool panels) {
     if (rotate) {
         switch (fmt) {
-        case E4M3: return launch_tr_fmt<E4M3, true>(x, rows, cols, ldx, sign_mask, codes, scales, stream);
-        case E5M2: return launch_tr_fmt<E5M2, true>(x, rows, cols, ldx, sign_mask, codes, scales, stream);
-        default: return launch_tr_fmt<E2M1, true>(x, rows, cols, ldx, sign_mask, codes, scales, stream);
+        case E4M3: return launch_tr_fmt<E4M3, true>(x, rows, cols, ldx, sign_mask, codes, scales, stream, panels);
+        case E5M2: return launch_tr_fmt<E5M2, true>(x, rows, cols, ldx, sign_mask, codes, scales, stream, panels);
+        default: return launch_tr_fmt<E2M1, true>(x, rows, cols, ldx, sign_mask, codes, scales, stream, panels);
         }
     }
     switch (fmt) {
-    case E4M3: return launch_tr_fmt<E4M3, false>(x, rows, cols, ldx, 0, codes, scales, stream);
-    case E5M2: return launch_tr_fmt<E5M2, false>(x, rows, cols, ldx, 0, codes, scales, stream);
-    default: return launch_tr_fmt<E2M1, false>(x, rows, cols, ldx, 0, codes, scales, stream);
+    case E4M3: return launch_tr_fmt<E4M3, false>(x, rows, cols, ldx, 0, codes, scales, stream, panels);
+    case E5M2: return launch_tr_fmt<E5M2, false>(x, rows, cols, ldx, 0, codes, scales, stream, panels);
+    default: return launch_tr_fmt<E2M1, false>(x, rows, cols, ldx, 0, codes, scales, stream, panels);
     }
 }
 
@@ -216,17 +222,18 @@ hipError_t launch_quantize_pair(int mode, int fmt, uint32_t sign_mask, const Qua
         default: return launch_rows_pair_fmt<E2M1>(a, b, stream);
         }
     }
-    if (mode == 2) {
+    const bool panels = mode >= 3;  // 3, 4: modes 1, 2 with K-panel output
+    if (mode == 2 || mode == 4) {
         switch (fmt) {
-        case E4M3: return launch_tr_pair_fmt<E4M3, true>(a, b, sign_mask, stream);
-        case E5M2: return launch_tr_pair_fmt<E5M2, true>(a, b, sign_mask, stream);
-        default: return launch_tr_pair_fmt<E2M1, true>(a, b, sign_mask, stream);
+        case E4M3: return launch_tr_pair_fmt<E4M3, true>(a, b, sign_mask, stream, panels);
+        case E5M2: return launch_tr_pair_fmt<E5M2, true>(a, b, sign_mask, stream, panels);
+        default: return launch_tr_pair_fmt<E2M1, true>(a, b, sign_mask, stream, panels);
         }
     }
     switch (fmt) {
-    case E4M3: return launch_tr_pair_fmt<E4M3, false>(a, b, 0, stream);
-    case E5M2: return launch_tr_pair_fmt<E5M2, false>(a, b, 0, stream);
-    default: return launch_tr_pair_fmt<E2M1, false>(a, b, 0, stream);
+    case E4M3: return launch_tr_pair_fmt<E4M3, false>(a, b, 0, stream, panels);
+    case E5M2: return launch_tr_pair_fmt<E5M2, false>(a, b, 0, stream, panels);
+    default: return launch_tr_pair_fmt<E2M1, false>(a, b, 0, stream, panels);
     }
 }
 

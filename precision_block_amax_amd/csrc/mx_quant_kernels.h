@@ -307,13 +307,20 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 // so that both operands of a GEMM take one launch; the grid's rows cover the
 // taller of the two, and a workgroup past its tensor's last row block writes
 // nothing.
+//
+// panels != 0 writes the transposed codes K-panel-major: the codes of output
+// row c that cover bytes [128 p, 128 p + 128) of the row (K elements
+// [256 p, 256 p + 256) for E2M1, [128 p, 128 p + 128) for FP8) sit at
+// codes + p * (cols * 128) + c * 128.  A workgroup's output then is whole
+// 32 KiB runs instead of 256 runs of 128 or 512 bytes (the GEMM reads either
+// layout; the launcher needs rows to be a whole number of panels).
 template <int F, bool ROTATE, bool VEC, int FR = -1, bool SR = false, bool PAIR = false>
 __global__ __launch_bounds__((64 * tr_waves<F, VEC, FR, SR>())) void k_quantize_transpose(
     const uint16_t *__restrict__ x, int64_t ldx, int64_t rows, int64_t cols, uint32_t sign_mask,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_r = nullptr,
     uint8_t *__restrict__ scales_r = nullptr, uint64_t seed = 0, const uint16_t *__restrict__ x1 = nullptr,
     int64_t ldx1 = 0, int64_t rows1 = 0, int64_t cols1 = 0, uint8_t *__restrict__ codes1 = nullptr,
-    uint8_t *__restrict__ scales1 = nullptr, uint32_t split = 0) {
+    uint8_t *__restrict__ scales1 = nullptr, uint32_t split = 0, int panels = 0) {
     static_assert(!(SR && FR >= 0), "stochastic rounding is a transposed-form variant");
     static_assert(!(PAIR && (SR || FR >= 0)), "pairs of the plain and rotated transposed forms only");
     constexpr int kTrWaves = tr_waves<F, VEC, FR, SR>(), kTrBlocks = kTrWaves;
@@ -507,7 +514,9 @@ __global__ __launch_bounds__((64 * tr_waves<F, VEC, FR, SR>())) void k_quantize_
         const int c = t / NCH, q = t % NCH;
         if (c >= nc || q >= vchunks) continue;
         const uint4 v = *reinterpret_cast<const uint4 *>(&sC[c * CB + ((q ^ key(c)) << 4)]);
-        uint8_t *dst = codes + (ctile + c) * row_bytes + rb0 * BB + q * 16;
+        const int64_t pos = rb0 * BB + q * 16;  // byte of output row ctile + c
+        uint8_t *dst = panels ? codes + (pos >> 7) * (cols * 128) + (ctile + c) * 128 + (pos & 127)
+                              : codes + (ctile + c) * row_bytes + pos;
         if (VEC) {
             *reinterpret_cast<uint4 *>(dst) = v;
         } else {

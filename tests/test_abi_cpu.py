@@ -30,6 +30,9 @@ def L():
     lib.mx_gemm.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, i64, P]
     lib.mx_quantize_strided.argtypes = [P, i64, i64, i64, i32, P, i64, P, i64, P]
     lib.mx_gemm_strided.argtypes = [P, i64, P, i64, i32, P, i64, P, i64, i32, i64, i64, i64, P, i32, i64, P]
+    lib.mx_quantize_transpose_panels.argtypes = [P, i64, i64, i64, i32, P, P, P]
+    lib.mx_hadamard32_quantize_panels.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
+    lib.mx_gemm_layout.argtypes = [P, i32, P, i32, P, i32, P, i32, i64, i64, i64, P, i32, i64, P]
     lib.mx_status_string.argtypes = [ctypes.c_int]
     lib.mx_status_string.restype = ctypes.c_char_p
     return lib
@@ -44,7 +47,8 @@ def test_exports_every_declared_function(L):
     names = declared_functions()
     assert {"mx_quantize", "mx_quantize_transpose", "mx_hadamard32_quantize", "mx_quantize_dual",
             "mx_quantize_transpose_sr", "mx_quantize_pair", "mx_gemm", "mx_quantize_strided",
-            "mx_gemm_strided", "mx_status_string", "mx_version"} <= set(names)
+            "mx_gemm_strided", "mx_quantize_transpose_panels", "mx_hadamard32_quantize_panels",
+            "mx_gemm_layout", "mx_status_string", "mx_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), "libmx.so does not export %s" % n
 
@@ -120,7 +124,8 @@ def test_pair_rejects(L):
                         k.get("x0", X), k.get("r0", 64), k.get("c0", 64), k.get("l0", 64), k.get("cd0", C),
                         k.get("s0", S), k.get("x1", X1), k.get("r1", 96), k.get("c1", 128), k.get("l1", 128),
                         k.get("cd1", C1), k.get("s1", S1), None]
-    assert f(*args(mode=3)) == INVALID                   # unknown mode
+    assert f(*args(mode=5)) == INVALID                   # unknown mode
+    assert f(*args(mode=-1)) == INVALID
     assert f(*args(fmt=7)) == INVALID
     assert f(*args(c1=48, l1=48)) == INVALID             # row mode: cols % 32 of the second tensor
     assert f(*args(mode=1, r0=48)) == INVALID            # transposed modes: rows % 32
@@ -132,6 +137,44 @@ def test_pair_rejects(L):
     assert f(*args(cd0=P(0x60000000))) == INVALID        # first codes over the second input
     assert f(*args(s1=P(0x10000040))) == INVALID         # second scales over the first input
     assert f(*args(r0=0, r1=0, x0=None, x1=None, cd0=None, s0=None, cd1=None, s1=None)) == OK  # both empty
+    # K-panel modes: rows a multiple of the panel width (128 FP8 elements, 256 E2M1)
+    assert f(*args(mode=3, r0=128, r1=96)) == INVALID
+    assert f(*args(mode=4, fmt=E2M1, r0=128, r1=256)) == INVALID
+    assert f(*args(mode=4, fmt=E2M1, r0=256, r1=256, cd1=P(0x20000100))) == INVALID   # overlap still checked
+    assert f(*args(mode=4, fmt=E2M1, r0=0, r1=0, x0=None, x1=None, cd0=None, s0=None, cd1=None, s1=None)) == OK
+
+
+@pytest.mark.parametrize("fn", ["mx_quantize_transpose_panels", "mx_hadamard32_quantize_panels"])
+def test_panel_quantize_rejects(L, fn):
+    f = getattr(L, fn)
+    rot = fn.startswith("mx_hadamard")
+    call = lambda x, r, c, ld, fmt, cd, sc: f(x, r, c, ld, *((0, fmt) if rot else (fmt,)), cd, sc, None)
+    assert call(X, 96, 4, 4, E4M3, C, S) == INVALID          # rows not a multiple of 128 (FP8 panel)
+    assert call(X, 128, 4, 4, E2M1, C, S) == INVALID         # rows not a multiple of 256 (E2M1 panel)
+    assert call(X, 128, 4, 4, 7, C, S) == INVALID            # format
+    assert call(X, 128, 4, 3, E4M3, C, S) == INVALID         # ldx < cols
+    assert call(X, 128, 4, 4, E4M3, X, S) == INVALID         # codes overlap x
+    assert call(X, 128, 4, 4, E4M3, None, S) == INVALID
+    assert call(None, 0, 4, 4, E4M3, None, None) == OK       # empty
+
+
+def test_gemm_layout_rejects(L):
+    f = L.mx_gemm_layout
+    A, AS, B, BS, Cc = (P(a) for a in (0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000))
+    ROWS, PANELS = 0, 1
+    args = lambda **k: [k.get("a", A), k.get("la", PANELS), AS, k.get("fa", E2M1), k.get("b", B), k.get("lb", PANELS),
+                        BS, k.get("fb", E2M1), k.get("M", 64), k.get("N", 64), k.get("K", 512), k.get("c", Cc), 0,
+                        k.get("ldc", 64), None]
+    assert f(*args(la=2)) == INVALID                           # unknown layout
+    assert f(*args(lb=-1)) == INVALID
+    assert f(*args(K=48)) == INVALID                           # mx_gemm's checks come first
+    assert f(*args(ldc=63)) == INVALID
+    assert f(*args(c=P(0x10000100))) == INVALID                # C overlaps A
+    assert f(*args(K=256)) == UNSUPPORTED                      # panels need K % 512 == 0
+    assert f(*args(a=P(0x10000008))) == UNSUPPORTED           # 16-byte aligned codes
+    assert f(*args(fb=E4M3, lb=ROWS)) == UNSUPPORTED           # an E2M1 panel operand needs an E2M1 partner
+    assert f(*args(M=1 << 23, K=1024, c=P(0x7000000000))) == UNSUPPORTED   # panel operand of 2^31 code bytes
+    assert f(*args(M=0, a=None, c=None)) == OK                 # empty
 
 
 def test_gemm_rejects(L):

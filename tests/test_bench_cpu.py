@@ -111,7 +111,7 @@ def test_summaries(profile_dirs):
 
 def test_kernel_symbols():
     assert bench.kernel_symbol("llama31_8b_gateup_fprop_mxfp4/Y mx_gemm e2m1xe2m1") == GEMM
-    assert bench.kernel_symbol("llama31_8b_wgrad_mxfp4_hadamard/dW mx_gemm e2m1xe2m1") == \
+    assert bench.kernel_symbol("llama31_8b_wgrad_mxfp4_hadamard/dW mx_gemm_layout e2m1xe2m1") == \
         "void mx::(anonymous namespace)::pipe::k_gemm_pipe<2, 2, false, 0>(mx::GemmArgs)"
     assert bench.kernel_symbol("llama31_8b_qkv_fprop_mxfp8/Y mx_gemm e4m3xe4m3") == \
         "void mx::(anonymous namespace)::pipe::k_gemm_pipe<0, 0, true, 1>(mx::GemmArgs)"

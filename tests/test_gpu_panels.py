@@ -1,0 +1,226 @@
+"""GPU parity of the K-panel code layout: the transposed quantizers writing
+their codes in panels (mx_quantize_transpose_panels,
+mx_hadamard32_quantize_panels, the panel modes of mx_quantize_pair) and the
+GEMM reading them in place (mx_gemm_layout).
+
+A panel operand of R rows and K elements holds K / P panels of R x 128 code
+bytes (P = 128 elements for FP8, 256 for E2M1): byte j of row r in panel p is
+byte 128 p + j of that row in the row-major layout.  So the oracle's row-major
+codes, cut into [R x K/P x 128] and transposed to [K/P x R x 128], are what
+the panel quantizers must write, byte for byte; scales stay row-major and must
+equal the oracle's.  The GEMM on panel operands must satisfy the same
+tolerance as mx_gemm against the oracle and, reading the same bytes in the
+same order, give exactly mx_gemm's output.  Covered: every format, with and
+without the rotation, ragged column tails, each operand alone in panels and
+both, ragged M and N, bf16 and fp32 output, the rejections of the layout
+call, and the full-size rotated MXFP4 weight-gradient GEMM
+(14336 x 4096 x 8192), every element.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import check_gemm, to_dev_bf16, to_dev_u8, to_host
+
+pytestmark = pytest.mark.gpu
+FMTS = ("e4m3", "e5m2", "e2m1")
+MASK = 0x9E3779B9
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import precision_block_amax_amd as m
+    m.lib()
+    return m
+
+
+def panel_elems(fmt):
+    return 256 if fmt == "e2m1" else 128
+
+
+def to_panels(codes: np.ndarray) -> np.ndarray:
+    """row-major codes [R x Kbytes] -> K-panel layout [Kbytes/128 x R x 128]"""
+    r, kb = codes.shape
+    assert kb % 128 == 0
+    return np.ascontiguousarray(codes.reshape(r, kb // 128, 128).transpose(1, 0, 2))
+
+
+def _bf16_bits(rng, rows, cols):
+    """normal values with ~1% of entries x40, rounded to bf16 (nearest, ties to even)"""
+    v = rng.standard_normal((rows, cols)).astype(np.float32)
+    v[rng.random((rows, cols)) < 0.01] *= 40.0
+    u = v.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _eq(got, want_codes, want_scales, what):
+    c, s = to_host(got[0]), to_host(got[1])
+    assert s.shape == want_scales.shape and np.array_equal(s, want_scales), "%s: scales differ" % what
+    assert c.shape == want_codes.shape and np.array_equal(c, want_codes), "%s: codes differ" % what
+
+
+# (rows, cols): rows span several panels; ragged column tails against the 64-column tile
+QSHAPES = ((512, 300), (1024, 1030), (256, 64))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("shape", QSHAPES)
+def test_panel_quantizers_match_oracle(mx, fmt, rotate, shape):
+    rows, cols = shape
+    rng = np.random.default_rng(rows + cols + 7 * FMTS.index(fmt) + int(rotate))
+    x = _bf16_bits(rng, rows, cols)
+    d = to_dev_bf16(x)
+    print("case", fmt, "rotate" if rotate else "plain", shape, flush=True)
+    want = oracle.hadamard32_quantize(x, fmt, MASK) if rotate else oracle.quantize_transpose(x, fmt)
+    got = (mx.hadamard32_quantize(d, fmt, MASK, layout="panels") if rotate
+           else mx.quantize_transpose(d, fmt, layout="panels"))
+    assert tuple(got[0].shape) == (mx.code_cols(rows, fmt) // 128, cols, 128)
+    _eq(got, to_panels(want[0]), want[1], "panel quantizer vs oracle")
+
+
+def test_panel_quantizer_strided_input_and_empty(mx):
+    """an input with a row stride above its width (the general, unvectorised path),
+    and an empty input"""
+    import torch
+    rng = np.random.default_rng(5)
+    x = _bf16_bits(rng, 256, 200)
+    full = to_dev_bf16(np.concatenate([x, np.zeros((256, 56), np.uint16)], axis=1))
+    view = full[:, :200]
+    want = oracle.hadamard32_quantize(x, "e2m1", MASK)
+    _eq(mx.hadamard32_quantize(view, "e2m1", MASK, layout="panels"), to_panels(want[0]), want[1], "strided input")
+    empty = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    c, s = mx.quantize_transpose(empty, "e4m3", layout="panels")
+    assert c.numel() == 0 and s.numel() == 0
+
+
+def test_panel_quantizer_rejects_ragged_panels(mx):
+    import torch
+    x = torch.zeros((384, 64), dtype=torch.bfloat16, device="cuda")  # 1.5 E2M1 panels
+    with pytest.raises(mx.MXError):
+        mx.quantize_transpose(x, "e2m1", layout="panels")
+    with pytest.raises(ValueError):
+        mx.quantize_transpose(x, "e4m3", layout="tiles")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("mode", ["transpose_panels", "hadamard_panels"])
+def test_pair_panel_modes(mx, fmt, mode):
+    """both tensors in one launch, different shapes (the second grid row range
+    outruns the shorter tensor), each equal to the oracle in panels and to the
+    single panel call"""
+    rng = np.random.default_rng(11 + FMTS.index(fmt) + (3 if mode.startswith("h") else 0))
+    x0, x1 = _bf16_bits(rng, 1024, 300), _bf16_bits(rng, 256, 260)
+    d0, d1 = to_dev_bf16(x0), to_dev_bf16(x1)
+    rot = mode.startswith("hadamard")
+    print("case", mode, fmt, flush=True)
+    p0, p1 = mx.quantize_pair(mode, d0, d1, fmt, MASK)
+    for p, x, d, what in ((p0, x0, d0, "first"), (p1, x1, d1, "second")):
+        want = oracle.hadamard32_quantize(x, fmt, MASK) if rot else oracle.quantize_transpose(x, fmt)
+        _eq(p, to_panels(want[0]), want[1], "%s tensor vs oracle" % what)
+        single = (mx.hadamard32_quantize(d, fmt, MASK, layout="panels") if rot
+                  else mx.quantize_transpose(d, fmt, layout="panels"))
+        _eq(p, to_host(single[0]), to_host(single[1]), "%s tensor vs single call" % what)
+
+
+def _rand_operand(rng, rows, K, fmt):
+    v = rng.standard_t(4, (rows, K)) * np.exp2(rng.integers(-6, 6, (rows, K // 32))).repeat(32, 1)
+    u = v.astype(np.float32).view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return oracle.quantize(bits, fmt)
+
+
+def _host_c(c, bf16):
+    h = to_host(c)
+    return workloads.bf16_bits_to_f32(h).astype(np.float64) if bf16 else h.astype(np.float64)
+
+
+# (fa, fb, which operands in panels): both E2M1 (the scaled FP4 kernel), FP8 pairs on
+# the carrier with either or both operands in panels, and an FP8 panel operand beside
+# a row-major E2M1 one
+GCASES = [("e2m1", "e2m1", (1, 1)), ("e2m1", "e2m1", (1, 0)), ("e2m1", "e2m1", (0, 1)),
+          ("e4m3", "e4m3", (1, 1)), ("e5m2", "e4m3", (0, 1)), ("e4m3", "e2m1", (1, 0))]
+
+
+@pytest.mark.parametrize("fa,fb,pan", GCASES)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_gemm_layout_matches_oracle_and_row_major(mx, fa, fb, pan, bf16):
+    import torch
+    M, N, K = 300, 520, 1024
+    rng = np.random.default_rng(GCASES.index((fa, fb, pan)) * 2 + int(bf16))
+    qa, qb = _rand_operand(rng, M, K, fa), _rand_operand(rng, N, K, fb)
+    C, S = oracle.gemm(qa[0], qa[1], fa, qb[0], qb[1], fb)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    ac = to_dev_u8(to_panels(qa[0]) if pan[0] else qa[0])
+    bc = to_dev_u8(to_panels(qb[0]) if pan[1] else qb[0])
+    print("case", fa, fb, pan, "bf16" if bf16 else "f32", flush=True)
+    c = mx.gemm(ac, to_dev_u8(qa[1]), fa, bc, to_dev_u8(qb[1]), fb, out_dtype=dt)
+    r = check_gemm(_host_c(c, bf16), C, S, bf16)
+    dense = mx.gemm(to_dev_u8(qa[0]), to_dev_u8(qa[1]), fa, to_dev_u8(qb[0]), to_dev_u8(qb[1]), fb, out_dtype=dt)
+    assert torch.equal(c.view(torch.int16 if bf16 else torch.int32), dense.view(torch.int16 if bf16 else torch.int32))
+    print("max |err|/S", r, flush=True)
+
+
+def test_gemm_layout_rows_is_mx_gemm_and_rejections(mx):
+    """both operands row-major through mx_gemm_layout is mx_gemm (any K); panel
+    operands on shapes the pipelined kernel does not take are rejected"""
+    import ctypes
+    import torch
+    rng = np.random.default_rng(3)
+    M, N, K = 70, 90, 352
+    qa, qb = _rand_operand(rng, M, K, "e4m3"), _rand_operand(rng, N, K, "e5m2")
+    dev = [to_dev_u8(t) for t in (qa[0], qa[1], qb[0], qb[1])]
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    L = mx.lib()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = L.mx_gemm_layout(ptr(dev[0]), 0, ptr(dev[1]), mx.E4M3, ptr(dev[2]), 0, ptr(dev[3]), mx.E5M2, M, N, K,
+                          ptr(out), mx.OUT_F32, N, None)
+    assert st == 0
+    want = mx.gemm(*dev[:2], "e4m3", *dev[2:], "e5m2", out_dtype=torch.float32)
+    assert torch.equal(out.view(torch.int32), want.view(torch.int32))
+    # K = 352 is not a multiple of 512: a panel operand is unsupported
+    st = L.mx_gemm_layout(ptr(dev[0]), 1, ptr(dev[1]), mx.E4M3, ptr(dev[2]), 0, ptr(dev[3]), mx.E5M2, M, N, K,
+                          ptr(out), mx.OUT_F32, N, None)
+    assert st == 2
+    # an E2M1 panel operand beside an FP8 one is unsupported
+    qa4 = _rand_operand(rng, M, 512, "e2m1")
+    qb8 = _rand_operand(rng, N, 512, "e4m3")
+    a4, as4, b8, bs8 = (to_dev_u8(t) for t in (to_panels(qa4[0]), qa4[1], qb8[0], qb8[1]))
+    with pytest.raises(mx.MXError):
+        mx.gemm(a4, as4, "e2m1", b8, bs8, "e4m3")
+
+
+def test_full_size_rotated_wgrad_in_panels(mx):
+    """the rotated MXFP4 weight-gradient GEMM of the Llama-3.1-8B down projection at
+    full size (M 14336, N 4096, K 8192 tokens): both operands quantized by the GPU in
+    one launch straight into panels, equal to the oracle's codes on every byte; the
+    GEMM on them equal to mx_gemm on the row-major codes and, every element, within
+    the tolerance of the oracle's product"""
+    import torch
+    cfg = workloads.config(3)
+    g = cfg.gemms[0]
+    qa_spec, qb_spec = cfg.quant(g.a), cfg.quant(g.b)
+    xa = workloads.draw_tensor(cfg, qa_spec.tensor)
+    xb = workloads.draw_tensor(cfg, qb_spec.tensor)
+    print("case", cfg.name, g.name, g.M, g.N, g.K, flush=True)
+    (ac, as_), (bc, bs) = mx.quantize_pair("hadamard_panels", to_dev_bf16(xa), to_dev_bf16(xb), "e2m1",
+                                          qa_spec.sign_mask)
+    qa = oracle.hadamard32_quantize(xa, "e2m1", qa_spec.sign_mask)
+    qb = oracle.hadamard32_quantize(xb, "e2m1", qb_spec.sign_mask)
+    _eq((ac, as_), to_panels(qa[0]), qa[1], "dY operand")
+    _eq((bc, bs), to_panels(qb[0]), qb[1], "X operand")
+    print("operands equal to the oracle", flush=True)
+    c = mx.gemm(ac, as_, "e2m1", bc, bs, "e2m1", out_dtype=torch.float32)
+    dense = mx.gemm(to_dev_u8(qa[0]), as_, "e2m1", to_dev_u8(qb[0]), bs, "e2m1", out_dtype=torch.float32)
+    assert torch.equal(c.view(torch.int32), dense.view(torch.int32))
+    ch = _host_c(c, False)
+    worst = 0.0
+    for r0 in range(0, g.M, 2048):
+        rows = np.arange(r0, min(g.M, r0 + 2048))
+        C, S = oracle.gemm(qa[0], qa[1], "e2m1", qb[0], qb[1], "e2m1", rows=rows)
+        worst = max(worst, check_gemm(ch[rows], C, S, False))
+        print("rows %d..%d checked" % (rows[0], rows[-1]), flush=True)
+    print("max |err|/S", worst, flush=True)
