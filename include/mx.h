@@ -317,6 +317,20 @@ mx_status_t mx_hadamard32_quantize_panels(const void *x_bf16, int64_t rows, int6
                                           void *stream);
 
 /*
+ * mx_quantize_dual_panels -- mx_quantize_dual (same arguments, codes and
+ * scales, same errors) with both forms' codes in the K-panel layout: the
+ * row form's (R = rows, K = cols) and the transposed form's (R = cols,
+ * K = rows).  cols must be a whole number of fmt_row panels and rows a whole
+ * number of fmt_t panels (else MX_ERR_INVALID_ARG).  A workgroup then writes
+ * each form as contiguous runs (4 KiB per wave of the row form, 32 KiB of
+ * the transposed one).  For callers: a linear layer whose GEMMs all read
+ * their operands in place through mx_gemm_layout.
+ */
+mx_status_t mx_quantize_dual_panels(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt_row,
+                                    void *codes_row, void *scales_row, mx_format_t fmt_t, int rotate,
+                                    uint32_t sign_mask, void *codes_t, void *scales_t, void *stream);
+
+/*
  * mx_gemm_layout -- mx_gemm with each operand's codes in the layout given
  * (a_layout, b_layout); scales dense.  With both MX_LAYOUT_ROWS it is
  * mx_gemm.  A K-panel operand needs the pipelined kernel: K a multiple of

@@ -64,10 +64,11 @@ def lib() -> ctypes.CDLL:
         L.mx_quantize_transpose_panels.argtypes = [P, i64, i64, i64, i32, P, P, P]
         L.mx_hadamard32_quantize_panels.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
         L.mx_gemm_layout.argtypes = [P, i32, P, i32, P, i32, P, i32, i64, i64, i64, P, i32, i64, P]
+        L.mx_quantize_dual_panels.argtypes = [P, i64, i64, i64, i32, P, P, i32, i32, u32, P, P, P]
         for fn in (L.mx_quantize, L.mx_quantize_transpose, L.mx_hadamard32_quantize, L.mx_quantize_dual,
                    L.mx_quantize_transpose_sr, L.mx_quantize_pair, L.mx_gemm, L.mx_quantize_strided,
                    L.mx_gemm_strided, L.mx_quantize_transpose_panels, L.mx_hadamard32_quantize_panels,
-                   L.mx_gemm_layout):
+                   L.mx_gemm_layout, L.mx_quantize_dual_panels):
             fn.restype = ctypes.c_int
         L.mx_status_string.argtypes = [ctypes.c_int]
         L.mx_status_string.restype = ctypes.c_char_p
@@ -214,17 +215,20 @@ def quantize_transpose(x: torch.Tensor, fmt, out=None, stream=None, layout: str 
 
 
 def quantize_dual(x: torch.Tensor, fmt_row, fmt_t, rotate: bool = False, sign_mask: int = 0, out=None,
-                  stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+                  stream=None, layout: str = "rows") -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     """mx_quantize_dual: (codes_row, scales_row, codes_t, scales_t) from one read of x; the row
     form as quantize(x, fmt_row), the transposed form as quantize_transpose(x, fmt_t) or, with
-    rotate, hadamard32_quantize(x, fmt_t, sign_mask).  `out` is a 4-tuple of output tensors."""
+    rotate, hadamard32_quantize(x, fmt_t, sign_mask).  `out` is a 4-tuple of output tensors.
+    layout="panels": mx_quantize_dual_panels, both forms' codes in the K-panel layout."""
     _check_bf16_2d(x)
     fr, ft = _fmt(fmt_row), _fmt(fmt_t)
     rows, cols = x.shape
-    cr, sr = _outputs(x.device, rows, cols, fr, None if out is None else out[:2])
-    ct, st = _outputs(x.device, cols, rows, ft, None if out is None else out[2:])
-    _check(lib().mx_quantize_dual(_ptr(x), rows, cols, _ldx(x), fr, _ptr(cr), _ptr(sr), ft, 1 if rotate else 0,
-                                  sign_mask & 0xFFFFFFFF, _ptr(ct), _ptr(st), _stream(x.device, stream)))
+    pan = _panels(layout)
+    cr, sr = _outputs(x.device, rows, cols, fr, None if out is None else out[:2], pan)
+    ct, st = _outputs(x.device, cols, rows, ft, None if out is None else out[2:], pan)
+    fn = lib().mx_quantize_dual_panels if pan else lib().mx_quantize_dual
+    _check(fn(_ptr(x), rows, cols, _ldx(x), fr, _ptr(cr), _ptr(sr), ft, 1 if rotate else 0, sign_mask & 0xFFFFFFFF,
+              _ptr(ct), _ptr(st), _stream(x.device, stream)))
     return cr, sr, ct, st
 
 

@@ -154,6 +154,29 @@ mx_status_t quantize_transpose_panels(const void *x_bf16, int64_t rows, int64_t 
                                                   (uint8_t *)codes, (uint8_t *)scales, (hipStream_t)stream, true));
 }
 
+// the fused dual-direction quantizer, with row-major or K-panel code outputs
+mx_status_t quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, int fr, void *codes_row,
+                          void *scales_row, int ft, int rotate, uint32_t sign_mask, void *codes_t, void *scales_t,
+                          void *stream, bool panels) {
+    if (rotate != 0 && rotate != 1) return MX_ERR_INVALID_ARG;
+    // K-panel outputs: each form's K (cols for the row form, rows for the transposed one) whole panels
+    if (panels && fmt_ok(fr) && fmt_ok(ft) && (cols % panel_elems(fr) != 0 || rows % panel_elems(ft) != 0))
+        return MX_ERR_INVALID_ARG;
+    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fr, codes_row, scales_row, false);
+    if (st != MX_OK) return st;
+    if ((st = check_quant(x_bf16, rows, cols, ldx, ft, codes_t, scales_t, true)) != MX_OK) return st;
+    if (rows == 0 || cols == 0) return MX_OK;
+    const int64_t n = rows * cols;
+    const int64_t crb = code_bytes(n, fr), ctb = code_bytes(n, ft), sb = n / 32;
+    if (overlap(codes_row, crb, codes_t, ctb) || overlap(codes_row, crb, scales_t, sb) ||
+        overlap(scales_row, sb, codes_t, ctb) || overlap(scales_row, sb, scales_t, sb))
+        return MX_ERR_INVALID_ARG;
+    if ((st = check_device()) != MX_OK) return st;
+    return launched(mx::launch_quantize_dual((const uint16_t *)x_bf16, rows, cols, ldx, fr, (uint8_t *)codes_row,
+                                             (uint8_t *)scales_row, ft, rotate != 0, sign_mask, (uint8_t *)codes_t,
+                                             (uint8_t *)scales_t, (hipStream_t)stream, panels));
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,22 +252,15 @@ mx_status_t mx_quantize_transpose_sr(const void *x_bf16, int64_t rows, int64_t c
 mx_status_t mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt_row,
                              void *codes_row, void *scales_row, mx_format_t fmt_t, int rotate, uint32_t sign_mask,
                              void *codes_t, void *scales_t, void *stream) {
-    const int fr = raw(fmt_row);
-    const int ft = raw(fmt_t);
-    if (rotate != 0 && rotate != 1) return MX_ERR_INVALID_ARG;
-    mx_status_t st = check_quant(x_bf16, rows, cols, ldx, fr, codes_row, scales_row, false);
-    if (st != MX_OK) return st;
-    if ((st = check_quant(x_bf16, rows, cols, ldx, ft, codes_t, scales_t, true)) != MX_OK) return st;
-    if (rows == 0 || cols == 0) return MX_OK;
-    const int64_t n = rows * cols;
-    const int64_t crb = code_bytes(n, fr), ctb = code_bytes(n, ft), sb = n / 32;
-    if (overlap(codes_row, crb, codes_t, ctb) || overlap(codes_row, crb, scales_t, sb) ||
-        overlap(scales_row, sb, codes_t, ctb) || overlap(scales_row, sb, scales_t, sb))
-        return MX_ERR_INVALID_ARG;
-    if ((st = check_device()) != MX_OK) return st;
-    return launched(mx::launch_quantize_dual((const uint16_t *)x_bf16, rows, cols, ldx, fr, (uint8_t *)codes_row,
-                                             (uint8_t *)scales_row, ft, rotate != 0, sign_mask, (uint8_t *)codes_t,
-                                             (uint8_t *)scales_t, (hipStream_t)stream));
+    return quantize_dual(x_bf16, rows, cols, ldx, raw(fmt_row), codes_row, scales_row, raw(fmt_t), rotate, sign_mask,
+                         codes_t, scales_t, stream, false);
+}
+
+mx_status_t mx_quantize_dual_panels(const void *x_bf16, int64_t rows, int64_t cols, int64_t ldx, mx_format_t fmt_row,
+                                    void *codes_row, void *scales_row, mx_format_t fmt_t, int rotate,
+                                    uint32_t sign_mask, void *codes_t, void *scales_t, void *stream) {
+    return quantize_dual(x_bf16, rows, cols, ldx, raw(fmt_row), codes_row, scales_row, raw(fmt_t), rotate, sign_mask,
+                         codes_t, scales_t, stream, true);
 }
 
 mx_status_t mx_quantize_pair(mx_pair_mode_t mode, mx_format_t fmt, uint32_t sign_mask, const void *x0,

@@ -47,7 +47,7 @@ hipError_t launch_quantize_transpose_sr(const uint16_t *x, int64_t rows, int64_t
 // one read of x: row form (fmt_r) and transposed form (fmt_t, rotated or not)
 hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx, int fmt_r,
                                 uint8_t *codes_r, uint8_t *scales_r, int fmt_t, bool rotate, uint32_t sign_mask,
-                                uint8_t *codes_t, uint8_t *scales_t, hipStream_t stream);
+                                uint8_t *codes_t, uint8_t *scales_t, hipStream_t stream, bool panels = false);
 
 // one tensor of a pair quantization: bf16 input [rows x ldx], outputs as the single call's
 struct QuantJob {

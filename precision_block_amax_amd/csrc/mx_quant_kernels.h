@@ -313,7 +313,10 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 // [256 p, 256 p + 256) for E2M1, [128 p, 128 p + 128) for FP8) sit at
 // codes + p * (cols * 128) + c * 128.  A workgroup's output then is whole
 // 32 KiB runs instead of 256 runs of 128 or 512 bytes (the GEMM reads either
-// layout; the launcher needs rows to be a whole number of panels).
+// layout; the launcher needs rows to be a whole number of panels).  With the
+// row form (FR >= 0) its codes go K-panel-major too: bytes [128 p, 128 p + 128)
+// of row r at codes_r + p * (rows * 128) + r * 128, so a wave's 32 rows are
+// one 4 KiB run per panel (cols a whole number of panels).
 template <int F, bool ROTATE, bool VEC, int FR = -1, bool SR = false, bool PAIR = false>
 __global__ __launch_bounds__((64 * tr_waves<F, VEC, FR, SR>())) void k_quantize_transpose(
     const uint16_t *__restrict__ x, int64_t ldx, int64_t rows, int64_t cols, uint32_t sign_mask,
@@ -483,7 +486,9 @@ __global__ __launch_bounds__((64 * tr_waves<F, VEC, FR, SR>())) void k_quantize_
                 const int t = k * 64 + lane, r = t / CPRr, q = t % CPRr;
                 if (q >= vcr) continue;
                 const uint4 v = *reinterpret_cast<const uint4 *>(&rc[r * RB + 16 * q]);
-                uint8_t *dst = codes_r + (rb * 32 + r) * rcb + ctile * RB / kTrCols + 16 * q;
+                const int64_t pos = ctile * RB / kTrCols + 16 * q;  // byte of row rb * 32 + r
+                uint8_t *dst = panels ? codes_r + (pos >> 7) * (rows * 128) + (rb * 32 + r) * 128 + (pos & 127)
+                                      : codes_r + (rb * 32 + r) * rcb + pos;
                 if (VEC) {
                     *reinterpret_cast<uint4 *>(dst) = v;
                 } else {

@@ -33,6 +33,7 @@ def L():
     lib.mx_quantize_transpose_panels.argtypes = [P, i64, i64, i64, i32, P, P, P]
     lib.mx_hadamard32_quantize_panels.argtypes = [P, i64, i64, i64, u32, i32, P, P, P]
     lib.mx_gemm_layout.argtypes = [P, i32, P, i32, P, i32, P, i32, i64, i64, i64, P, i32, i64, P]
+    lib.mx_quantize_dual_panels.argtypes = [P, i64, i64, i64, i32, P, P, i32, i32, u32, P, P, P]
     lib.mx_status_string.argtypes = [ctypes.c_int]
     lib.mx_status_string.restype = ctypes.c_char_p
     return lib
@@ -48,7 +49,7 @@ def test_exports_every_declared_function(L):
     assert {"mx_quantize", "mx_quantize_transpose", "mx_hadamard32_quantize", "mx_quantize_dual",
             "mx_quantize_transpose_sr", "mx_quantize_pair", "mx_gemm", "mx_quantize_strided",
             "mx_gemm_strided", "mx_quantize_transpose_panels", "mx_hadamard32_quantize_panels",
-            "mx_gemm_layout", "mx_status_string", "mx_version"} <= set(names)
+            "mx_gemm_layout", "mx_quantize_dual_panels", "mx_status_string", "mx_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), "libmx.so does not export %s" % n
 
@@ -156,6 +157,20 @@ def test_panel_quantize_rejects(L, fn):
     assert call(X, 128, 4, 4, E4M3, X, S) == INVALID         # codes overlap x
     assert call(X, 128, 4, 4, E4M3, None, S) == INVALID
     assert call(None, 0, 4, 4, E4M3, None, None) == OK       # empty
+
+
+def test_dual_panels_rejects(L):
+    f = L.mx_quantize_dual_panels
+    args = lambda **k: [k.get("x", X), k.get("rows", 256), k.get("cols", 256), k.get("ldx", 256), k.get("fr", E2M1),
+                        k.get("cr", C), k.get("sr", S), k.get("ft", E2M1), k.get("rot", 1), 0, k.get("ct", C2),
+                        k.get("st", S2), None]
+    assert f(*args(cols=224, ldx=224)) == INVALID       # row form: cols not whole E2M1 panels
+    assert f(*args(rows=128)) == INVALID                 # transposed form: rows not whole E2M1 panels
+    assert f(*args(fr=E4M3, cols=320, ldx=320)) == INVALID   # not whole FP8 panels (128)
+    assert f(*args(rot=2)) == INVALID
+    assert f(*args(ct=C)) == INVALID                     # the two code buffers overlap
+    assert f(*args(ft=9)) == INVALID
+    assert f(*args(rows=0, x=None, cr=None, sr=None, ct=None, st=None)) == OK
 
 
 def test_gemm_layout_rejects(L):

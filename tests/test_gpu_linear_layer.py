@@ -78,3 +78,39 @@ def test_layer_gemm_sampled_rows(layer, gname):
         C, S = oracle.gemm(ra[0][rows], ra[1][rows], qa.fmt, rb[0][n0:n1], rb[1][n0:n1], qb.fmt)
         worst = max(worst, check_gemm(got[:, n0:n1], C, S, bf16))
     print("max |err|/S", worst, flush=True)
+
+
+def _to_panels(codes: np.ndarray) -> np.ndarray:
+    """row-major codes [R x Kbytes] -> K-panel layout [Kbytes/128 x R x 128]"""
+    r, kb = codes.shape
+    return np.ascontiguousarray(codes.reshape(r, kb // 128, 128).transpose(1, 0, 2))
+
+
+@pytest.mark.timeout(600)
+def test_layer_in_k_panels(layer):
+    """the same layer with every operand in the K-panel layout (mx_quantize_dual_panels):
+    both forms of every tensor equal to the oracle's codes cut into panels, byte for
+    byte, and each GEMM through mx_gemm_layout bit-identical to mx_gemm on the
+    row-major operands above"""
+    import torch
+    mx, ops, ref = layer
+    pops = {}
+    for src, q_row, q_t in workloads.LAYER_DUALS:
+        bits = workloads.draw_tensor(CFG, src)
+        qr, qt = CFG.quant(q_row), CFG.quant(q_t)
+        print("dual quantize in panels %s %s" % (src, bits.shape), flush=True)
+        cr, sr, ct, st = mx.quantize_dual(to_dev_bf16(bits), qr.fmt, qt.fmt, qt.kind == "hadamard", MASK,
+                                          layout="panels")
+        pops[q_row], pops[q_t] = (cr, sr), (ct, st)
+        for q, (c, s) in ((q_row, (cr, sr)), (q_t, (ct, st))):
+            assert np.array_equal(to_host(s), ref[q][1]), "%s scales" % q
+            assert np.array_equal(to_host(c), _to_panels(ref[q][0])), "%s codes" % q
+    for g in CFG.gemms:
+        qa, qb = CFG.quant(g.a), CFG.quant(g.b)
+        dt = torch.bfloat16 if g.out == "bf16" else torch.float32
+        print("case", g.name, g.M, g.N, g.K, flush=True)
+        c = mx.gemm(pops[g.a][0], pops[g.a][1], qa.fmt, pops[g.b][0], pops[g.b][1], qb.fmt, out_dtype=dt)
+        d = mx.gemm(ops[g.a][0], ops[g.a][1], qa.fmt, ops[g.b][0], ops[g.b][1], qb.fmt, out_dtype=dt)
+        iv = torch.int16 if dt == torch.bfloat16 else torch.int32
+        assert torch.equal(c.view(iv), d.view(iv)), g.name
+        del c, d

@@ -1,7 +1,8 @@
 """GPU parity of the K-panel code layout: the transposed quantizers writing
 their codes in panels (mx_quantize_transpose_panels,
-mx_hadamard32_quantize_panels, the panel modes of mx_quantize_pair) and the
-GEMM reading them in place (mx_gemm_layout).
+mx_hadamard32_quantize_panels, the panel modes of mx_quantize_pair), the
+fused dual quantizer writing both forms in panels (mx_quantize_dual_panels)
+and the GEMM reading them in place (mx_gemm_layout).
 
 A panel operand of R rows and K elements holds K / P panels of R x 128 code
 bytes (P = 128 elements for FP8, 256 for E2M1): byte j of row r in panel p is
@@ -124,6 +125,27 @@ def test_pair_panel_modes(mx, fmt, mode):
         single = (mx.hadamard32_quantize(d, fmt, MASK, layout="panels") if rot
                   else mx.quantize_transpose(d, fmt, layout="panels"))
         _eq(p, to_host(single[0]), to_host(single[1]), "%s tensor vs single call" % what)
+
+
+DUAL_FMTS = [("e2m1", "e2m1"), ("e4m3", "e4m3"), ("e4m3", "e2m1"), ("e2m1", "e5m2")]
+
+
+@pytest.mark.parametrize("fr,ft", DUAL_FMTS)
+@pytest.mark.parametrize("rotate", [False, True])
+def test_dual_panels_match_oracle(mx, fr, ft, rotate):
+    """mx_quantize_dual_panels: the row form and the (rotated) transposed form, each
+    equal to the oracle's codes cut into panels and to its scales, for row counts of
+    several workgroup row spans; with an FP8 row form, 640 columns leave the last
+    256-column tile half full"""
+    rng = np.random.default_rng(31 + DUAL_FMTS.index((fr, ft)) * 2 + int(rotate))
+    rows, cols = 512, (768 if fr == "e2m1" else 640)
+    x = _bf16_bits(rng, rows, cols)
+    print("case", fr, ft, "rotate" if rotate else "plain", flush=True)
+    cr, sr, ct, st = mx.quantize_dual(to_dev_bf16(x), fr, ft, rotate, MASK, layout="panels")
+    wr = oracle.quantize(x, fr)
+    wt = oracle.hadamard32_quantize(x, ft, MASK) if rotate else oracle.quantize_transpose(x, ft)
+    _eq((cr, sr), to_panels(wr[0]), wr[1], "row form")
+    _eq((ct, st), to_panels(wt[0]), wt[1], "transposed form")
 
 
 def _rand_operand(rng, rows, K, fmt):
