@@ -13,9 +13,9 @@ equal the oracle's.  The GEMM on panel operands must satisfy the same
 tolerance as mx_gemm against the oracle and, reading the same bytes in the
 same order, give exactly mx_gemm's output.  Covered: every format, with and
 without the rotation, ragged column tails, each operand alone in panels and
-both, ragged M and N, bf16 and fp32 output, the rejections of the layout
-call, and the full-size rotated MXFP4 weight-gradient GEMM
-(14336 x 4096 x 8192), every element.
+both, ragged M and N, bf16 and fp32 output, the carrier's byte-0 block check
+reading panel codes, the rejections of the layout call, and the full-size
+rotated MXFP4 weight-gradient GEMM (14336 x 4096 x 8192), every element.
 """
 import numpy as np
 import pytest
@@ -184,6 +184,51 @@ def test_gemm_layout_matches_oracle_and_row_major(mx, fa, fb, pan, bf16):
     dense = mx.gemm(to_dev_u8(qa[0]), to_dev_u8(qa[1]), fa, to_dev_u8(qb[0]), to_dev_u8(qb[1]), fb, out_dtype=dt)
     assert torch.equal(c.view(torch.int16 if bf16 else torch.int32), dense.view(torch.int16 if bf16 else torch.int32))
     print("max |err|/S", r, flush=True)
+
+
+def _random_codes(rng, rows, K, fmt):
+    """uniform random code bytes; FP8 NaN (E4M3) and Inf/NaN (E5M2) codes replaced by 1.0"""
+    if fmt == "e2m1":
+        return rng.integers(0, 256, (rows, K // 2)).astype(np.uint8)
+    c = rng.integers(0, 256, (rows, K)).astype(np.uint8)
+    c[((c & 0x7F) == 0x7F) if fmt == "e4m3" else ((c & 0x7C) == 0x7C)] = 0x38
+    return c
+
+
+@pytest.mark.parametrize("fa,fb,pan", [("e4m3", "e4m3", (1, 1)), ("e5m2", "e4m3", (0, 1)), ("e4m3", "e2m1", (1, 0))])
+@pytest.mark.parametrize("case", ["zero_blocks", "tiny_blocks"])
+def test_gemm_layout_carrier_blocks_under_scale_zero(mx, fa, fb, pan, case):
+    """the carrier's pre-check reads the codes of byte-0 blocks (rows whose other
+    blocks lie 100+ binades higher) in the panel layout: all-zero blocks keep the
+    fast path, blocks of tiny nonzero values must send their tile to the exact
+    kernel; C within the tolerance of the oracle and equal to mx_gemm's on the
+    row-major codes"""
+    import torch
+    rng = np.random.default_rng(71 + ["zero_blocks", "tiny_blocks"].index(case) * 10 + FMTS.index(fa) + 3 * FMTS.index(fb))
+    M, N, K = 300, 272, 1024
+    kb = K // 32
+    ca, cb = _random_codes(rng, M, K, fa), _random_codes(rng, N, K, fb)
+    sa = rng.integers(98, 128, (M, kb)).astype(np.uint8)
+    sb = rng.integers(98, 128, (N, kb)).astype(np.uint8)
+    for c, s, fmt, rows in ((ca, sa, fa, np.arange(0, M, 2)), (cb, sb, fb, np.arange(1, N, 5))):
+        nb = 16 if fmt == "e2m1" else 32
+        for r, b in zip(rows, rng.integers(0, kb, rows.size)):
+            s[r, b] = 0
+            c[r, b * nb:(b + 1) * nb] = (0x88 if fmt == "e2m1" else 0x80) if r % 3 == 0 else 0
+    if case == "tiny_blocks":
+        for r in (4, 130, 262):
+            sa[r, int(rng.integers(0, kb))] = 0
+    C, S = oracle.gemm(ca, sa, fa, cb, sb, fb)
+    print("case", case, fa, fb, pan, flush=True)
+    for bf16 in (False, True):
+        dt = torch.bfloat16 if bf16 else torch.float32
+        got = mx.gemm(to_dev_u8(to_panels(ca) if pan[0] else ca), to_dev_u8(sa), fa,
+                      to_dev_u8(to_panels(cb) if pan[1] else cb), to_dev_u8(sb), fb, out_dtype=dt)
+        dense = mx.gemm(to_dev_u8(ca), to_dev_u8(sa), fa, to_dev_u8(cb), to_dev_u8(sb), fb, out_dtype=dt)
+        iv = torch.int16 if bf16 else torch.int32
+        assert torch.equal(got.view(iv), dense.view(iv))
+        r = check_gemm(_host_c(got, bf16), C, S, bf16)
+        print(case, "bf16" if bf16 else "f32", "max |err|/S", r, flush=True)
 
 
 def test_gemm_layout_rows_is_mx_gemm_and_rejections(mx):
