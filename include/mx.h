@@ -33,7 +33,8 @@
  *     accumulation).  Inputs and outputs must not overlap.
  *   - bf16 inputs are row-major with a leading dimension `ldx` (elements
  *     between the starts of consecutive rows, ldx >= cols).
- *   - Outputs are dense row-major:
+ *   - Outputs are dense row-major (the _panels calls and pair modes write
+ *     their codes in the K-panel layout described before them instead):
  *       FP8 codes   : one byte per element;
  *       E2M1 codes  : two elements per byte, element 2i in bits 3:0 and
  *                     element 2i+1 in bits 7:4;
