@@ -112,6 +112,18 @@ def measured_clock(kernel: str):
     return None if data is None else data.get("sclk_ghz", {}).get(kernel)
 
 
+def pair_layout(qs, shapes):
+    """How a GEMM's quantize calls run: (pair, panels).  Both operands go in one
+    mx_quantize_pair launch when they share mode, format and sign mask; a
+    transposed or rotated pair writes its codes in the K-panel layout when both
+    tensors' rows are whole panels (256 elements for E2M1, 128 for FP8), and the
+    GEMM then reads that layout in place (mx_gemm_layout)."""
+    pair = len(qs) == 2 and len({(q.kind, q.fmt, q.sign_mask) for q in qs}) == 1
+    panels = pair and qs[0].kind != "row" and all(
+        shp[0] % (256 if q.fmt == "e2m1" else 128) == 0 for q, shp in zip(qs, shapes))
+    return pair, panels
+
+
 class Step:
     """device buffers and the ordered kernel launches of one step"""
 
@@ -128,10 +140,7 @@ class Step:
             cfg = workloads.config(ci)
             tens = {t.name: bf16(cfg, t.name) for t in cfg.tensors}
             qs = cfg.quants
-            pair = len(qs) == 2 and len({(q.kind, q.fmt, q.sign_mask) for q in qs}) == 1
-            # a transposed pair writes its codes in the K-panel layout, which the GEMM reads in place
-            panels = pair and qs[0].kind != "row" and all(
-                tens[q.tensor].shape[0] % (256 if q.fmt == "e2m1" else 128) == 0 for q in qs)
+            pair, panels = pair_layout(qs, [tuple(tens[q.tensor].shape) for q in qs])
             ops = {}
             for q in cfg.quants:
                 x = tens[q.tensor]
@@ -407,9 +416,10 @@ def _device_tensor(torch, spec, gen):
 
 
 def llama70b_set(mx, torch, seed: int, reps: int = 3) -> dict:
-    """The Llama-3.1-70B single-layer linear set at 8192 tokens: each GEMM's two
-    quantize calls and the GEMM, back to back, per launch (median of `reps`
-    passes).  Eight of the nine GEMMs have FP8 operands and run on the bf16
+    """The Llama-3.1-70B single-layer linear set at 8192 tokens: each GEMM's
+    quantize launches (one pair launch where both operands share a mode, as in
+    the step; else two calls) and the GEMM, back to back, per launch (median of
+    `reps` passes).  Eight of the nine GEMMs have FP8 operands and run on the bf16
     carrier; they are reported against the bf16 matrix peak it runs on and
     against MXFP8's."""
     cfg = workloads.config(4)
@@ -418,17 +428,28 @@ def llama70b_set(mx, torch, seed: int, reps: int = 3) -> dict:
     out, total_ms, total_flops, quant_ms, quant_bytes_ = [], 0.0, 0.0, 0.0, 0.0
     for g in cfg.gemms:
         launches, ops = [], {}
-        for qn in (g.a, g.b):
-            q = cfg.quant(qn)
+        qs = (cfg.quant(g.a), cfg.quant(g.b))
+        pair, panels = pair_layout(qs, [tuple(dev[q.tensor].shape) for q in qs])
+        for q in qs:
             x = dev[q.tensor]
             rows, k = (x.shape[0], x.shape[1]) if q.kind == "row" else (x.shape[1], x.shape[0])
-            c = torch.empty((rows, mx.code_cols(k, q.fmt)), dtype=torch.uint8, device="cuda")
+            shape = (mx.code_cols(k, q.fmt) // 128, rows, 128) if panels else (rows, mx.code_cols(k, q.fmt))
+            c = torch.empty(shape, dtype=torch.uint8, device="cuda")
             sc = torch.empty((rows, k // 32), dtype=torch.uint8, device="cuda")
-            ops[qn] = (c, sc, q.fmt)
-            fn = {"row": lambda x=x, q=q, c=c, sc=sc: mx.quantize(x, q.fmt, out=(c, sc)),
-                  "transpose": lambda x=x, q=q, c=c, sc=sc: mx.quantize_transpose(x, q.fmt, out=(c, sc)),
-                  "hadamard": lambda x=x, q=q, c=c, sc=sc: mx.hadamard32_quantize(x, q.fmt, 0, out=(c, sc))}[q.kind]
-            launches.append(("%s %s %s" % (qn, q.kind, q.fmt), fn, quant_bytes(x.shape[0], x.shape[1], q.fmt)))
+            ops[q.name] = (c, sc, q.fmt)
+            if not pair:
+                fn = {"row": lambda x=x, q=q, c=c, sc=sc: mx.quantize(x, q.fmt, out=(c, sc)),
+                      "transpose": lambda x=x, q=q, c=c, sc=sc: mx.quantize_transpose(x, q.fmt, out=(c, sc)),
+                      "hadamard": lambda x=x, q=q, c=c, sc=sc: mx.hadamard32_quantize(
+                          x, q.fmt, q.sign_mask, out=(c, sc))}[q.kind]
+                launches.append(("%s %s %s" % (q.name, q.kind, q.fmt), fn, quant_bytes(x.shape[0], x.shape[1], q.fmt)))
+        if pair:
+            q0, q1 = qs
+            mode = q0.kind + ("_panels" if panels else "")
+            fn = (lambda mode=mode, q0=q0, x0=dev[q0.tensor], x1=dev[q1.tensor], o0=ops[q0.name][:2],
+                  o1=ops[q1.name][:2]: mx.quantize_pair(mode, x0, x1, q0.fmt, q0.sign_mask, out0=o0, out1=o1))
+            launches.append(("%s+%s pair %s %s" % (q0.name, q1.name, mode, q0.fmt), fn,
+                             sum(quant_bytes(*dev[q.tensor].shape, q.fmt) for q in qs)))
         a, b = ops[g.a], ops[g.b]
         cbuf = torch.empty((g.M, g.N), dtype=torch.bfloat16 if g.out == "bf16" else torch.float32, device="cuda")
         launches.append(("%s gemm" % g.name, lambda a=a, b=b, cbuf=cbuf: mx.gemm(
@@ -437,21 +458,22 @@ def llama70b_set(mx, torch, seed: int, reps: int = 3) -> dict:
             fn()
         torch.cuda.synchronize()
         t, _ = _time_sequence(torch, [(n, fn) for n, fn, _ in launches], reps)
+        gi = len(launches) - 1  # the GEMM; the quantize launches before it
         arith = "fp4" if a[2] == "e2m1" and b[2] == "e2m1" else "bf16"
-        tf = launches[2][2] / (t[2] * 1e-3) / 1e12
-        r = {"gemm": g.name, "M": g.M, "N": g.N, "K": g.K, "formats": "%sx%s" % (a[2], b[2]), "ms": round(t[2], 4),
+        tf = launches[gi][2] / (t[gi] * 1e-3) / 1e12
+        r = {"gemm": g.name, "M": g.M, "N": g.N, "K": g.K, "formats": "%sx%s" % (a[2], b[2]), "ms": round(t[gi], 4),
              "TFLOPs": round(tf, 1), "arith": arith, "frac": round(tf / PEAK_TFLOPS[arith], 4),
              "quantize": [{"call": launches[k][0], "ms": round(t[k], 4),
                            "GBps": round(launches[k][2] / (t[k] * 1e-3) / 1e9, 1),
                            "frac_of_hbm_peak": round(launches[k][2] / (t[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
-                          for k in (0, 1)]}
+                          for k in range(gi)]}
         if arith == "bf16":
             r["frac_of_mxfp8_peak"] = round(tf / PEAK_TFLOPS["fp8"], 4)
         out.append(r)
-        total_ms += t[2]
-        total_flops += launches[2][2]
-        quant_ms += t[0] + t[1]
-        quant_bytes_ += launches[0][2] + launches[1][2]
+        total_ms += t[gi]
+        total_flops += launches[gi][2]
+        quant_ms += sum(t[:gi])
+        quant_bytes_ += sum(w for _, _, w in launches[:gi])
         del launches, ops, cbuf, a, b
     return {"gemms": out, "gemm_ms_total": round(total_ms, 3),
             "gemm_TFLOPs_aggregate": round(total_flops / (total_ms * 1e-3) / 1e12, 1),
@@ -459,7 +481,8 @@ def llama70b_set(mx, torch, seed: int, reps: int = 3) -> dict:
             "quantize_GBps_aggregate": round(quant_bytes_ / (quant_ms * 1e-3) / 1e9, 1),
             "inputs": "drawn on the device with the recipe's shapes and distributions (timing only; the parity "
                       "tests use the seeded host draws)",
-            "how": "each GEMM after its two quantize calls, back to back; median of %d passes" % reps}
+            "how": "each GEMM after its operands' quantize launches (one pair launch where both share a "
+                   "mode), back to back; median of %d passes" % reps}
 
 
 def _read_csv(path):

@@ -12,10 +12,17 @@ column, within |err| <= 1e-5 * sum |a*b| (plus half a bf16 ulp for bf16
 output); the oracle's fp64 product runs over column chunks of B so that its
 dequantized operand stays bounded in host memory.  Checking all 8192 rows of
 the 32 TFLOP set takes the oracle minutes on many host cores, which is why C
-is sampled by rows while the operands are compared in full."""
+is sampled by rows while the operands are compared in full.
+
+Where the benchmark quantizes a GEMM's two operands in one pair launch (both
+in one mode; rotated pairs in the K-panel layout), that launch runs too: its
+outputs must equal the single calls' outputs above, byte for byte (cut into
+panels where it writes panels), and the GEMM is then run on them, as the
+benchmark runs it."""
 import numpy as np
 import pytest
 
+import bench
 import oracle
 import workloads
 from helpers import check_gemm, to_dev_bf16, to_host
@@ -91,6 +98,18 @@ def test_70b_gemm(mx, gname):
     b_ref = oracle_quant(qb)
     assert_operand_equal(qb.name, b_gpu, b_ref)
     print("operand %s: every code and scale equal" % qb.name, flush=True)
+
+    pair, panels = bench.pair_layout((qa, qb), (tensor(qa.tensor)[0].shape, tensor(qb.tensor)[0].shape))
+    if pair:
+        mode = qa.kind + ("_panels" if panels else "")
+        pa, pb = mx.quantize_pair(mode, tensor(qa.tensor)[1], tensor(qb.tensor)[1], qa.fmt, qa.sign_mask)
+        for got, single, name in ((pa, a_gpu, qa.name), (pb, b_gpu, qb.name)):
+            want = single[0]
+            if panels:  # row-major [R x Kbytes] -> [Kbytes/128 x R x 128]
+                want = want.view(want.shape[0], want.shape[1] // 128, 128).permute(1, 0, 2).contiguous()
+            assert torch.equal(got[0], want) and torch.equal(got[1], single[1]), "%s: pair launch" % name
+        print("pair launch %s: both operands equal to the single calls" % mode, flush=True)
+        a_gpu, b_gpu = pa, pb
 
     bf16 = g.out == "bf16"
     c = mx.gemm(a_gpu[0], a_gpu[1], qa.fmt, b_gpu[0], b_gpu[1], qb.fmt,
