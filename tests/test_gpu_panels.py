@@ -83,16 +83,27 @@ def test_panel_quantizers_match_oracle(mx, fmt, rotate, shape):
     _eq(got, to_panels(want[0]), want[1], "panel quantizer vs oracle")
 
 
-def test_panel_quantizer_strided_input_and_empty(mx):
-    """an input with a row stride above its width (the general, unvectorised path),
-    and an empty input"""
+@pytest.mark.parametrize("pad", [56, 3])
+def test_panel_quantizer_strided_input_and_empty(mx, pad):
+    """inputs with a row stride above their width: 256 elements (the vectorised
+    path) and 203 elements (not a multiple of 4: the general, unvectorised path,
+    whose stores go byte by byte), for the rotated quantizer and the dual; and an
+    empty input"""
     import torch
-    rng = np.random.default_rng(5)
+    rng = np.random.default_rng(5 + pad)
     x = _bf16_bits(rng, 256, 200)
-    full = to_dev_bf16(np.concatenate([x, np.zeros((256, 56), np.uint16)], axis=1))
+    full = to_dev_bf16(np.concatenate([x, np.zeros((256, pad), np.uint16)], axis=1))
     view = full[:, :200]
+    assert view.stride(0) == 200 + pad
     want = oracle.hadamard32_quantize(x, "e2m1", MASK)
     _eq(mx.hadamard32_quantize(view, "e2m1", MASK, layout="panels"), to_panels(want[0]), want[1], "strided input")
+    # the dual: a row form of 200 columns is not whole panels, so its input keeps 256 columns
+    xd = _bf16_bits(rng, 256, 256)
+    fulld = to_dev_bf16(np.concatenate([xd, np.zeros((256, pad), np.uint16)], axis=1))
+    cr, sr, ct, st = mx.quantize_dual(fulld[:, :256], "e4m3", "e2m1", True, MASK, layout="panels")
+    wr, wt = oracle.quantize(xd, "e4m3"), oracle.hadamard32_quantize(xd, "e2m1", MASK)
+    _eq((cr, sr), to_panels(wr[0]), wr[1], "dual row form, strided input")
+    _eq((ct, st), to_panels(wt[0]), wt[1], "dual transposed form, strided input")
     empty = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     c, s = mx.quantize_transpose(empty, "e4m3", layout="panels")
     assert c.numel() == 0 and s.numel() == 0
