@@ -173,9 +173,10 @@ def _host_c(c, bf16):
 
 # (fa, fb, which operands in panels): both E2M1 (the scaled FP4 kernel), FP8 pairs on
 # the carrier with either or both operands in panels, and an FP8 panel operand beside
-# a row-major E2M1 one
+# a row-major E2M1 one, as A and as B
 GCASES = [("e2m1", "e2m1", (1, 1)), ("e2m1", "e2m1", (1, 0)), ("e2m1", "e2m1", (0, 1)),
-          ("e4m3", "e4m3", (1, 1)), ("e5m2", "e4m3", (0, 1)), ("e4m3", "e2m1", (1, 0))]
+          ("e4m3", "e4m3", (1, 1)), ("e5m2", "e4m3", (0, 1)), ("e4m3", "e2m1", (1, 0)),
+          ("e2m1", "e5m2", (0, 1))]
 
 
 @pytest.mark.parametrize("fa,fb,pan", GCASES)
@@ -240,6 +241,19 @@ def test_gemm_layout_carrier_blocks_under_scale_zero(mx, fa, fb, pan, case):
         assert torch.equal(got.view(iv), dense.view(iv))
         r = check_gemm(_host_c(got, bf16), C, S, bf16)
         print(case, "bf16" if bf16 else "f32", "max |err|/S", r, flush=True)
+
+
+def test_gemm_layout_k_zero(mx):
+    """K = 0 with panel operands (no panels at all): C = 0, as mx_gemm writes it"""
+    import torch
+    M, N = 70, 300
+    a = torch.empty((0, M, 128), dtype=torch.uint8, device="cuda")
+    b = torch.empty((0, N, 128), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, 0), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N, 0), dtype=torch.uint8, device="cuda")
+    out = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    c = mx.gemm(a, sa, "e2m1", b, sb, "e2m1", out_dtype=torch.float32, out=out)
+    assert torch.count_nonzero(c).item() == 0
 
 
 def test_gemm_layout_rows_is_mx_gemm_and_rejections(mx):
