@@ -31,45 +31,27 @@ template <> struct Traits<E4M3> { static constexpr int EMAX = 8; };    // 448 = 
 template <> struct Traits<E5M2> { static constexpr int EMAX = 15; };   // 57344 = 1.75 * 2^15
 template <> struct Traits<E2M1> { static constexpr int EMAX = 2; };    // 6 = 1.5 * 2^2
 
-MXHD int clz32(uint32_t v) {  // v != 0
-#if defined(__HIP_DEVICE_COMPILE__)
-    return __clz(v);
-#else
-    return __builtin_clz(v);
-#endif
-}
-
 // ---------------------------------------------------------------------------
 // Block scale exponent e = clamp(floor(log2 amax) - EMAX, -127, 127).
+//
+// For a finite amax this is max(E - bias - EMAX, -127), E the amax's exponent
+// field: a normal amax has floor(log2 amax) = E - bias; a subnormal one (E = 0)
+// or zero lies below 2^(1 - bias) <= 2^-126, so its exponent reaches the lower
+// clamp anyway, as E = 0 gives; and E <= 254 keeps e <= 127 - EMAX, below the
+// upper clamp.  No leading-zero count and no branch.
 
 // amax given as bf16 magnitude bits (bits & 0x7FFF), finite.
 template <int F>
 MXHD int scale_exp_bf16(uint32_t amax_bits) {
-    int fl;
-    if (amax_bits >= 0x80u)
-        fl = (int)(amax_bits >> 7) - 127;          // normal: exponent field - bias
-    else if (amax_bits == 0u)
-        return -127;                               // all-zero block
-    else
-        fl = (31 - clz32(amax_bits)) - 133;        // subnormal: m * 2^-133
-    int e = fl - Traits<F>::EMAX;
-    e = e < -127 ? -127 : e;
-    return e > 127 ? 127 : e;
+    const int e = (int)(amax_bits >> 7) - 127 - Traits<F>::EMAX;
+    return e < -127 ? -127 : e;
 }
 
 // amax given as fp32 magnitude bits (bits & 0x7FFFFFFF), finite.
 template <int F>
 MXHD int scale_exp_f32(uint32_t amax_bits) {
-    int fl;
-    if (amax_bits >= 0x00800000u)
-        fl = (int)(amax_bits >> 23) - 127;
-    else if (amax_bits == 0u)
-        return -127;
-    else
-        fl = (31 - clz32(amax_bits)) - 149;        // subnormal: m * 2^-149
-    int e = fl - Traits<F>::EMAX;
-    e = e < -127 ? -127 : e;
-    return e > 127 ? 127 : e;
+    const int e = (int)(amax_bits >> 23) - 127 - Traits<F>::EMAX;
+    return e < -127 ? -127 : e;
 }
 
 }  // namespace mx
