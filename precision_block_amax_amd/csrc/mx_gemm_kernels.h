@@ -865,7 +865,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
     // issue_next() sends the next stage's loads (to the other buffer) once this
     // stage's first LDS reads are out, so that their issue overlaps the reads'
     // latency instead of delaying them
-    auto compute = [&](auto S, auto T, auto P, auto &&issue_next) {
+    auto compute = [&](auto S, auto T, auto P, bool cur_live, auto &&issue_next) {
         const uint8_t *tA = stA(S), *tB = stB(S);
         const uint8_t *tSA = stS(T, 0) + SBY * decltype(P)::value, *tSB = stS(T, 1) + SBY * decltype(P)::value;
         if constexpr (MODE == 0) {
@@ -921,29 +921,32 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
         } else if constexpr (MODE == 1) {
             // Per row, the stage's four block exponents rebased on the row's reference:
             // byte q = S_q - R + 127, which lies in [87, 127] for real blocks (scale spread
-            // <= 40 binades, S_q <= R), so 2^(S_q - R) <= 1 is the float with that byte
-            // as its exponent field.  Stages past the end of K and rows past the edge of
-            // the matrix hold zero codes and zero scale bytes, whose bytes wrap; the
-            // scale is clamped to 1 so that they stay finite and add exactly 0 (an
-            // exponent byte of 255 would be Inf, and 0 * Inf a NaN).
+            // <= 40 binades, S_q <= R; an all-zero block under byte 0 only stays on this
+            // path while R <= 127), so 2^(S_q - R) <= 1 is the float with that byte as its
+            // exponent field.  A stage past the end of K holds zero codes and zero scale
+            // bytes, whose rebased bytes would wrap (255 is Inf, and 0 * Inf a NaN): it
+            // takes scale 1 instead, so its terms add exactly 0.  Rows past the edge of
+            // the matrix may wrap too, but they only reach rows and columns of C that are
+            // not stored.
             const auto rebase = [](uint32_t w, int R) -> uint32_t {
                 const uint32_t rr = __builtin_amdgcn_perm(0u, (uint32_t)R, 0u);  // R in every byte
                 return w - rr + 0x7F7F7F7Fu;  // bytewise S_q + 127 - R, no carries for real blocks
             };
             const auto block_scale = [](uint32_t d, int q) -> float {
-                const uint32_t b = ((d >> (8 * q)) & 0xFFu) << 23;
-                return __uint_as_float(b < 0x3F800000u ? b : 0x3F800000u);
+                return __uint_as_float(((d >> (8 * q)) & 0xFFu) << 23);
             };
             uint32_t da[4], db[2];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int ra_ = wm * 128 + i * 32 + l32;
-                da[i] = rebase(*reinterpret_cast<const uint32_t *>(&tSA[ra_ * 16]), sRa[ra_]);
+                const uint32_t d = rebase(*reinterpret_cast<const uint32_t *>(&tSA[ra_ * 16]), sRa[ra_]);
+                da[i] = cur_live ? d : 0x7F7F7F7Fu;
             }
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 const int rb_ = wn * 64 + j * 32 + l32;
-                db[j] = rebase(*reinterpret_cast<const uint32_t *>(&tSB[rb_ * 16]), sRb[rb_]);
+                const uint32_t d = rebase(*reinterpret_cast<const uint32_t *>(&tSB[rb_ * 16]), sRb[rb_]);
+                db[j] = cur_live ? d : 0x7F7F7F7Fu;
             }
             // Software-pipelined: the codes of a step pair are read from LDS (one 16-byte
             // read per fragment) at the top of the step before the pair, and step t + 1's
@@ -1048,7 +1051,7 @@ __global__ __launch_bounds__(PNT, 1) void k_gemm_pipe(GemmArgs g) {
             // here would let the compiler sink the stage's MFMAs past the next
             // barrier and keep every fragment of the stage live across it
             compute(std::integral_constant<int, u % 2>{}, std::integral_constant<int, u / SPS>{},
-                    std::integral_constant<int, u % SPS>{}, [&] {
+                    std::integral_constant<int, u % SPS>{}, kt < ntk, [&] {
                         issue(std::integral_constant<int, (u + 1) % 2>{},
                               std::integral_constant<int, ((u + 1) / SPS) % 2>{},
                               std::integral_constant<bool, (u + 1) % SPS == 0>{}, kt + 1);
